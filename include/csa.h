@@ -1,0 +1,202 @@
+/*
+ * csa.h -- C ABI of libcsa, the MI355X (gfx950) compressed-sparse-attention
+ * decode path: lightning-indexer scoring, causal top-k, gather, and shared-KV
+ * MQA attention (plus the dense HCA variant), as described by the
+ * nvfp4-megamoe-kernel design notes "ARCHITECTURE & MEMORY AUDIT" (post-probe
+ * rewrite and the earlier 1M-context-viability audit) and "PART A -- Next
+ * Session Clues".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 tensors are passed as uint16_t bit patterns.
+ * - Every tensor pointer is a DEVICE pointer owned by the caller; layouts are
+ *   row-major with the last index fastest and no padding.  Pointers to bf16
+ *   and fp32 tensors must be 16-byte aligned.
+ * - Per-token metadata arrays (pos, seq_kv, n_comp, ...) are device arrays of
+ *   length T.  Caches of several sequences are concatenated ("packed"); token
+ *   t's sequence starts at row seq_kv[t].
+ * - Visible blocks of token t: n_vis[t] = min(floor(pos[t] / ratio), n_comp[t])
+ *   -- a decode query sees only compressed blocks strictly before its own,
+ *   incomplete block (PART A, suspect 3).
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *   The library never allocates, frees or synchronises; it holds no global
+ *   mutable state and is reentrant.  Scratch memory is the caller's `ws`.
+ * - Host-side validation happens before any launch and returns CSA_EINVAL /
+ *   CSA_EUNSUPPORTED / CSA_EWORKSPACE without touching the GPU.  A failed launch
+ *   returns CSA_EHIP.  Conditions that only the device can see (a row index
+ *   outside its buffer, more visible blocks than `ld`, ...) never cause an
+ *   out-of-bounds access: the kernel skips or clamps the offending item and ORs
+ *   a CSA_DERR_* bit into *err (a device uint32 word, may be NULL; never
+ *   cleared by the library).
+ * - There is no silent fallback: an unsupported shape is an error.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum csa_status {
+  CSA_OK = 0,
+  CSA_EINVAL = 1,        /* null required pointer, negative size, bad value   */
+  CSA_EUNSUPPORTED = 2,  /* shape outside the compiled set (see each call)    */
+  CSA_EWORKSPACE = 3,    /* ws NULL, misaligned (256 B) or smaller than needed */
+  CSA_EHIP = 4           /* the HIP runtime rejected a launch                  */
+} csa_status;
+
+/* Device-side error bits ORed into *err. */
+#define CSA_DERR_VIS_OVER_LD   0x1u  /* n_vis[t] > ld: only the first ld scores kept      */
+#define CSA_DERR_KEY_RANGE     0x2u  /* seq_kv[t]+n_vis[t] > k_rows: token scored as 0 blocks */
+#define CSA_DERR_BAD_META      0x4u  /* pos < 0 or n_comp < 0 or seq_kv < 0              */
+#define CSA_DERR_ROW_RANGE     0x8u  /* gather/attend row outside its buffer: row zeroed / skipped */
+#define CSA_DERR_COUNT_RANGE   0x10u /* count > top_k or swa_len > window: clamped        */
+#define CSA_DERR_ROWS_OVER_MAX 0x20u /* a_len+b_len > max_rows: rows beyond max_rows ignored */
+
+/* Human-readable name of a csa_status value. */
+const char* csa_status_str(int status);
+
+/* Version of this ABI (bumped on any signature change). */
+int csa_abi_version(void);
+
+/*
+ * S1 -- lightning-indexer scores (post-probe audit, F1 and F3; eq. 16 of
+ * DeepSeek-V4 sec. 2.3.1 as restated there):
+ *     scores[t, s] = sum_{h < n_ih} w[t,h] * max(0, sum_{d < ihd} q_idx[t,h,d] * k_idx[seq_kv[t]+s, d])
+ * for s < n_vis[t].  One key per block, shared by every indexer head.
+ *   q_idx  [T, n_ih, ihd] bf16     w [T, n_ih] fp32
+ *   k_idx  [k_rows, ihd] bf16      (packed keys of all sequences)
+ *   scores [T, ld] fp32            entries s >= n_vis[t] are not written
+ * bf16 products are accumulated in fp32 (MFMA); ReLU, weighting and the head
+ * sum are fp32.  Supported: ihd in {32, 64, 128}; 1 <= n_ih <= 128;
+ * ratio >= 1; ld >= 1; T >= 0 (T == 0 is a no-op).
+ */
+csa_status csa_index_score(const uint16_t* q_idx, const float* w,
+                           const uint16_t* k_idx, int64_t k_rows,
+                           const int64_t* pos, const int64_t* seq_kv, const int32_t* n_comp,
+                           int T, int n_ih, int ihd, int ratio,
+                           float* scores, int64_t ld, uint32_t* err, void* stream);
+
+/*
+ * S2 -- causal top-k (post-probe audit, F3: tk = min(top_k, n_comp), topk over
+ * the scores; PART A suspect 3: only blocks before the query's own block).
+ * For each token, k_eff = min(top_k, n_vis[t]) indices s < n_vis[t] of the
+ * largest scores[t, s] are written to idx[t, 0:k_eff] in ascending block order;
+ * idx[t, k_eff:top_k] = -1; count[t] = k_eff.  Among equal scores the lower
+ * block index wins, so the result is deterministic.  Comparison is on the fp32
+ * values (-0.0 == +0.0).  NaN scores are not supported.
+ *   scores [T, ld] fp32 (entries s < n_vis[t] read)
+ *   idx    [T, top_k] int32      count [T] int32
+ *   ws     >= csa_topk_workspace_bytes(T, ld, top_k) bytes, 256-B aligned;
+ *          contents on entry are irrelevant.
+ * Supported: 1 <= top_k <= 2048, ld >= 1.
+ */
+size_t csa_topk_workspace_bytes(int T, int64_t ld, int top_k);
+csa_status csa_topk(const float* scores, int64_t ld,
+                    const int64_t* pos, const int32_t* n_comp,
+                    int T, int ratio, int top_k,
+                    int32_t* idx, int32_t* count,
+                    void* ws, size_t ws_bytes, uint32_t* err, void* stream);
+
+/*
+ * S3 -- gather into one preallocated buffer (post-probe audit, B1/B2 and C2;
+ * 1M-context audit, D3/D5): row j < count[t] of all_kv[t] is
+ * comp_kv[seq_kv[t] + idx[t,j]]; rows count[t] .. count[t]+swa_len[t]-1 are
+ * swa[swa_row0[t] + i].  n_kv[t] = count[t] + swa_len[t].  Rows of all_kv[t]
+ * at or beyond n_kv[t] are left untouched.  Bit-exact copy.
+ *   comp_kv [comp_rows, head_dim] bf16     swa [swa_rows, head_dim] bf16
+ *   idx [T, top_k] int32   count [T] int32   swa_row0 [T] int64  swa_len [T] int32
+ *   all_kv  [T, top_k + window, head_dim] bf16     n_kv [T] int32
+ * Supported: head_dim in {64, 128, 256, 512}; top_k >= 0; window >= 0.
+ */
+csa_status csa_gather(const uint16_t* comp_kv, int64_t comp_rows, const int64_t* seq_kv,
+                      const int32_t* idx, const int32_t* count, int top_k,
+                      const uint16_t* swa, int64_t swa_rows,
+                      const int64_t* swa_row0, const int32_t* swa_len, int window,
+                      int T, int head_dim,
+                      uint16_t* all_kv, int32_t* n_kv, uint32_t* err, void* stream);
+
+/*
+ * S4 -- shared-KV MQA softmax attention (post-probe audit, F3 "shared key-value
+ * MQA"; 1M-context audit, D4 for the dense HCA row set and D6 for the sink).
+ * Token t attends over segment A rows kv_a[a_row0[t] .. a_row0[t]+a_len[t]-1]
+ * followed by segment B rows kv_b[b_row0[t] .. +b_len[t]-1]; each row is both
+ * key and value:
+ *     z_j = scale * q[t,h] . row_j
+ *     out[t,h] = sum_j e^{z_j} row_j / (sum_j e^{z_j} + [sink] e^{sink[h]})
+ *     lse[t,h] = log(sum_j e^{z_j} + [sink] e^{sink[h]})
+ * bf16 MFMA products, fp32 softmax and accumulation, bf16 output.  An empty row
+ * set without sink gives out = 0 and lse = -inf.
+ *   q [T, n_heads, head_dim] bf16   out [T, n_heads, head_dim] bf16
+ *   lse [T, n_heads] fp32 or NULL   sink [n_heads] fp32 or NULL
+ *   kv_b, b_row0, b_len may all be NULL (one segment).
+ *   max_rows: host bound on a_len[t] + b_len[t] (sizes the split grid).
+ *   ws >= csa_attend_workspace_bytes(T, n_heads, head_dim, max_rows), 256-B aligned.
+ * Supported: head_dim in {64, 128, 256, 512}; 1 <= n_heads <= 128; max_rows >= 0.
+ */
+size_t csa_attend_workspace_bytes(int T, int n_heads, int head_dim, int max_rows);
+csa_status csa_mqa_attend(const uint16_t* q, int T, int n_heads, int head_dim,
+                          float scale, const float* sink,
+                          const uint16_t* kv_a, int64_t a_rows,
+                          const int64_t* a_row0, const int32_t* a_len,
+                          const uint16_t* kv_b, int64_t b_rows,
+                          const int64_t* b_row0, const int32_t* b_len,
+                          int max_rows, uint16_t* out, float* lse,
+                          void* ws, size_t ws_bytes, uint32_t* err, void* stream);
+
+/*
+ * S5 -- one decode step of one attention layer, all stages enqueued on one
+ * stream with no host synchronisation (capturable in a HIP graph).
+ *
+ * mode CSA_MODE_CSA: S1 -> S2 -> S3 -> S4 over all_kv (selected compressed rows,
+ *   then SWA rows).  Requires q_idx, w, k_idx, all_kv.
+ * mode CSA_MODE_HCA (1M-context audit, D4): no indexer; S4 over the entire
+ *   visible compressed history comp_kv[seq_kv[t] .. +n_vis[t]-1] followed by
+ *   the SWA rows, read in place (no concatenation).
+ *
+ * Optional outputs (NULL = kept in the workspace): scores [T, max_vis],
+ * idx [T, top_k], count [T], n_kv [T], lse [T, n_heads].
+ * max_vis is the host bound on n_vis[t] over the batch.
+ */
+enum { CSA_MODE_CSA = 0, CSA_MODE_HCA = 1 };
+
+typedef struct csa_step_args {
+  int mode;
+  int T, n_ih, ihd, ratio, top_k, window, n_heads, head_dim;
+  int64_t max_vis;
+  float scale;
+  const uint16_t* q_idx;    /* [T, n_ih, ihd]        (CSA) */
+  const float* w;           /* [T, n_ih]             (CSA) */
+  const uint16_t* k_idx;    /* [k_rows, ihd]         (CSA) */
+  int64_t k_rows;
+  const uint16_t* comp_kv;  /* [comp_rows, head_dim] */
+  int64_t comp_rows;
+  const uint16_t* swa;      /* [swa_rows, head_dim]  */
+  int64_t swa_rows;
+  const uint16_t* q;        /* [T, n_heads, head_dim] */
+  const float* sink;        /* [n_heads] or NULL     */
+  const int64_t* pos;       /* [T] */
+  const int64_t* seq_kv;    /* [T] */
+  const int32_t* n_comp;    /* [T] */
+  const int64_t* swa_row0;  /* [T] */
+  const int32_t* swa_len;   /* [T] */
+  uint16_t* all_kv;         /* [T, top_k + window, head_dim]  (CSA, required) */
+  uint16_t* out;            /* [T, n_heads, head_dim] (required) */
+  float* lse;               /* [T, n_heads] or NULL  */
+  float* scores;            /* [T, max_vis] or NULL  */
+  int32_t* idx;             /* [T, top_k] or NULL    */
+  int32_t* count;           /* [T] or NULL           */
+  int32_t* n_kv;            /* [T] or NULL           */
+  uint32_t* err;            /* device word or NULL   */
+} csa_step_args;
+
+size_t csa_decode_step_workspace_bytes(const csa_step_args* a);
+csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

@@ -1,0 +1,294 @@
+// C ABI of libcsa: argument validation, workspace carving and stage
+// sequencing.  Every check here runs on the host before any launch; nothing
+// in this file allocates, frees or synchronises.
+#include <math.h>
+
+#include "csa_common.h"
+
+using namespace csa;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxGridY = 65535;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+csa_status hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EHIP; }
+
+csa_status check_index(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                       int64_t k_rows, const int64_t* pos, const int64_t* seq_kv,
+                       const int32_t* n_comp, int T, int n_ih, int ihd, int ratio,
+                       const float* scores, int64_t ld) {
+  if (T < 0 || n_ih < 1 || ratio < 1 || ld < 1 || k_rows < 0) return CSA_EINVAL;
+  if (!q_idx || !w || !k_idx || !pos || !seq_kv || !n_comp || !scores) return CSA_EINVAL;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned4(w) || !aligned4(scores))
+    return CSA_EINVAL;
+  if (ihd != 32 && ihd != 64 && ihd != 128) return CSA_EUNSUPPORTED;
+  if (n_ih > 128 || T > kMaxGridY || ld > INT32_MAX) return CSA_EUNSUPPORTED;
+  return CSA_OK;
+}
+
+csa_status check_topk(const float* scores, int64_t ld, const int64_t* pos,
+                      const int32_t* n_comp, int T, int ratio, int top_k, const int32_t* idx,
+                      const int32_t* count) {
+  if (T < 0 || ld < 1 || ratio < 1 || top_k < 1) return CSA_EINVAL;
+  if (!scores || !pos || !n_comp || !idx || !count) return CSA_EINVAL;
+  if (!aligned16(scores)) return CSA_EINVAL;
+  if (top_k > kMaxTopk || T > kMaxGridY || ld > INT32_MAX) return CSA_EUNSUPPORTED;
+  return CSA_OK;
+}
+
+csa_status check_gather(const uint16_t* comp_kv, int64_t comp_rows, const int64_t* seq_kv,
+                        const int32_t* idx, const int32_t* count, int top_k,
+                        const uint16_t* swa, int64_t swa_rows, const int64_t* swa_row0,
+                        const int32_t* swa_len, int window, int T, int head_dim,
+                        const uint16_t* all_kv, const int32_t* n_kv) {
+  if (T < 0 || top_k < 0 || window < 0 || comp_rows < 0 || swa_rows < 0) return CSA_EINVAL;
+  if (!comp_kv || !seq_kv || !idx || !count || !swa || !swa_row0 || !swa_len || !all_kv || !n_kv)
+    return CSA_EINVAL;
+  if (!aligned16(comp_kv) || !aligned16(swa) || !aligned16(all_kv)) return CSA_EINVAL;
+  if (!head_dim_ok(head_dim)) return CSA_EUNSUPPORTED;
+  if (T > kMaxGridY || top_k > kMaxTopk || window > 1024) return CSA_EUNSUPPORTED;
+  return CSA_OK;
+}
+
+csa_status check_attend(const uint16_t* q, int T, int n_heads, int head_dim, float scale,
+                        const uint16_t* kv_a, int64_t a_rows, const uint16_t* kv_b,
+                        int64_t b_rows, const int64_t* b_row0, const int32_t* b_len,
+                        int max_rows, const uint16_t* out) {
+  if (T < 0 || n_heads < 1 || max_rows < 0 || a_rows < 0 || b_rows < 0) return CSA_EINVAL;
+  if (!q || !kv_a || !out || !isfinite(scale)) return CSA_EINVAL;
+  const bool any_b = kv_b || b_row0 || b_len;
+  const bool all_b = kv_b && b_row0 && b_len;
+  if (any_b && !all_b) return CSA_EINVAL;
+  if (!aligned16(q) || !aligned16(kv_a) || (kv_b && !aligned16(kv_b))) return CSA_EINVAL;
+  if (!head_dim_ok(head_dim)) return CSA_EUNSUPPORTED;
+  if (n_heads > 128 || T > kMaxGridY) return CSA_EUNSUPPORTED;
+  return CSA_OK;
+}
+
+csa_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return CSA_OK;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < need)
+    return CSA_EWORKSPACE;
+  return CSA_OK;
+}
+
+// Workspace of a decode step, in carve order.
+struct StepWs {
+  size_t scores, topk, idx, count, n_kv, attend, total;
+};
+
+StepWs step_ws_layout(const csa_step_args* a) {
+  StepWs w{};
+  size_t off = 0;
+  if (a->mode == CSA_MODE_CSA) {
+    w.scores = off;
+    if (!a->scores) off += align256((size_t)a->T * (size_t)a->max_vis * 4);
+    w.topk = off;
+    off += topk_ws_bytes(a->T, a->max_vis);
+    w.idx = off;
+    if (!a->idx) off += align256((size_t)a->T * a->top_k * 4);
+    w.count = off;
+    if (!a->count) off += align256((size_t)a->T * 4);
+    w.n_kv = off;
+    if (!a->n_kv) off += align256((size_t)a->T * 4);
+    w.attend = off;
+    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, a->top_k + a->window);
+  } else {
+    w.attend = off;
+    const int64_t rows = a->max_vis + a->window;
+    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, rows > INT32_MAX ? INT32_MAX : (int)rows);
+  }
+  w.total = off;
+  return w;
+}
+
+csa_status check_step(const csa_step_args* a) {
+  if (!a) return CSA_EINVAL;
+  if (a->mode != CSA_MODE_CSA && a->mode != CSA_MODE_HCA) return CSA_EINVAL;
+  if (a->T < 0 || a->max_vis < 0 || a->window < 0 || a->ratio < 1 || a->n_heads < 1)
+    return CSA_EINVAL;
+  if (a->comp_rows < 0 || a->swa_rows < 0) return CSA_EINVAL;
+  if (!a->q || !a->out || !a->comp_kv || !a->swa || !a->pos || !a->seq_kv || !a->n_comp ||
+      !a->swa_row0 || !a->swa_len)
+    return CSA_EINVAL;
+  if (!isfinite(a->scale)) return CSA_EINVAL;
+  if (!aligned16(a->q) || !aligned16(a->comp_kv) || !aligned16(a->swa) || !aligned16(a->out))
+    return CSA_EINVAL;
+  if (!head_dim_ok(a->head_dim) || a->n_heads > 128 || a->T > kMaxGridY || a->window > 1024)
+    return CSA_EUNSUPPORTED;
+  if (a->max_vis + a->window > INT32_MAX) return CSA_EUNSUPPORTED;
+  if (a->mode == CSA_MODE_CSA) {
+    if (!a->q_idx || !a->w || !a->k_idx || !a->all_kv) return CSA_EINVAL;
+    if (a->n_ih < 1 || a->top_k < 1 || a->max_vis < 1 || a->k_rows < 0) return CSA_EINVAL;
+    if (!aligned16(a->q_idx) || !aligned16(a->k_idx) || !aligned16(a->all_kv) || !aligned4(a->w))
+      return CSA_EINVAL;
+    if ((a->scores && !aligned16(a->scores)) || (a->idx && !aligned4(a->idx)) ||
+        (a->count && !aligned4(a->count)) || (a->n_kv && !aligned4(a->n_kv)))
+      return CSA_EINVAL;
+    if (a->ihd != 32 && a->ihd != 64 && a->ihd != 128) return CSA_EUNSUPPORTED;
+    if (a->n_ih > 128 || a->top_k > kMaxTopk) return CSA_EUNSUPPORTED;
+  }
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_str(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_EINVAL: return "CSA_EINVAL: invalid argument";
+    case CSA_EUNSUPPORTED: return "CSA_EUNSUPPORTED: shape outside the supported set";
+    case CSA_EWORKSPACE: return "CSA_EWORKSPACE: workspace missing, misaligned or too small";
+    case CSA_EHIP: return "CSA_EHIP: HIP launch failed";
+    default: return "unknown csa_status";
+  }
+}
+
+int csa_abi_version(void) { return kAbiVersion; }
+
+csa_status csa_index_score(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                           int64_t k_rows, const int64_t* pos, const int64_t* seq_kv,
+                           const int32_t* n_comp, int T, int n_ih, int ihd, int ratio,
+                           float* scores, int64_t ld, uint32_t* err, void* stream) {
+  csa_status s = check_index(q_idx, w, k_idx, k_rows, pos, seq_kv, n_comp, T, n_ih, ihd, ratio,
+                             scores, ld);
+  if (s != CSA_OK || T == 0) return s;
+  IndexScoreLaunch L{q_idx, w, k_idx, k_rows, pos, seq_kv, n_comp, T, n_ih, ihd, ratio,
+                     scores, ld, nullptr, err};
+  return hip_status(launch_index_score(L, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_topk_workspace_bytes(int T, int64_t ld, int top_k) {
+  (void)top_k;
+  if (T <= 0 || ld <= 0) return 0;
+  return topk_ws_bytes(T, ld);
+}
+
+csa_status csa_topk(const float* scores, int64_t ld, const int64_t* pos, const int32_t* n_comp,
+                    int T, int ratio, int top_k, int32_t* idx, int32_t* count, void* ws,
+                    size_t ws_bytes, uint32_t* err, void* stream) {
+  csa_status s = check_topk(scores, ld, pos, n_comp, T, ratio, top_k, idx, count);
+  if (s != CSA_OK || T == 0) return s;
+  s = check_ws(ws, ws_bytes, topk_ws_bytes(T, ld));
+  if (s != CSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const TopkWs tw = topk_ws_carve(ws, T, ld);
+  const int64_t nz = (reinterpret_cast<char*>(tw.cand) - reinterpret_cast<char*>(tw.hist)) / 4;
+  hipError_t e = launch_zero_u32(tw.hist, nz, st);
+  if (e == hipSuccess) e = launch_score_hist(scores, ld, pos, n_comp, T, ratio, tw.hist, err, st);
+  if (e == hipSuccess)
+    e = launch_topk_select(scores, ld, pos, n_comp, T, ratio, top_k, idx, count, tw, err, st);
+  return hip_status(e);
+}
+
+csa_status csa_gather(const uint16_t* comp_kv, int64_t comp_rows, const int64_t* seq_kv,
+                      const int32_t* idx, const int32_t* count, int top_k, const uint16_t* swa,
+                      int64_t swa_rows, const int64_t* swa_row0, const int32_t* swa_len,
+                      int window, int T, int head_dim, uint16_t* all_kv, int32_t* n_kv,
+                      uint32_t* err, void* stream) {
+  csa_status s = check_gather(comp_kv, comp_rows, seq_kv, idx, count, top_k, swa, swa_rows,
+                              swa_row0, swa_len, window, T, head_dim, all_kv, n_kv);
+  if (s != CSA_OK || T == 0) return s;
+  GatherLaunch L{comp_kv, comp_rows, seq_kv, idx, count, top_k, swa, swa_rows, swa_row0,
+                 swa_len, window, T, head_dim, all_kv, n_kv, err};
+  return hip_status(launch_gather(L, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_attend_workspace_bytes(int T, int n_heads, int head_dim, int max_rows) {
+  if (T <= 0 || n_heads <= 0 || !head_dim_ok(head_dim) || max_rows < 0) return 0;
+  return attend_ws_bytes(T, n_heads, head_dim, max_rows);
+}
+
+csa_status csa_mqa_attend(const uint16_t* q, int T, int n_heads, int head_dim, float scale,
+                          const float* sink, const uint16_t* kv_a, int64_t a_rows,
+                          const int64_t* a_row0, const int32_t* a_len, const uint16_t* kv_b,
+                          int64_t b_rows, const int64_t* b_row0, const int32_t* b_len,
+                          int max_rows, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                          uint32_t* err, void* stream) {
+  csa_status s = check_attend(q, T, n_heads, head_dim, scale, kv_a, a_rows, kv_b, b_rows, b_row0,
+                              b_len, max_rows, out);
+  if (s != CSA_OK) return s;
+  if (!a_row0 || !a_len) return CSA_EINVAL;
+  if (T == 0) return CSA_OK;
+  s = check_ws(ws, ws_bytes, attend_ws_bytes(T, n_heads, head_dim, max_rows));
+  if (s != CSA_OK) return s;
+  AttendLaunch L{};
+  L.q = q; L.T = T; L.n_heads = n_heads; L.head_dim = head_dim; L.scale = scale; L.sink = sink;
+  L.kv_a = kv_a; L.a_rows = a_rows; L.a_row0 = a_row0; L.a_len = a_len; L.a_stride = 0;
+  L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
+  L.kv_b = kv_b; L.b_rows = b_rows; L.b_row0 = b_row0; L.b_len = b_len;
+  L.max_rows = max_rows; L.out = out; L.lse = lse; L.ws = ws; L.err = err;
+  return hip_status(launch_attend(L, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_decode_step_workspace_bytes(const csa_step_args* a) {
+  if (check_step(a) != CSA_OK) return 0;
+  return step_ws_layout(a).total;
+}
+
+csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream) {
+  csa_status s = check_step(a);
+  if (s != CSA_OK) return s;
+  if (a->T == 0) return CSA_OK;
+  const StepWs lay = step_ws_layout(a);
+  s = check_ws(ws, ws_bytes, lay.total);
+  if (s != CSA_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+
+  AttendLaunch L{};
+  L.q = a->q; L.T = a->T; L.n_heads = a->n_heads; L.head_dim = a->head_dim;
+  L.scale = a->scale; L.sink = a->sink; L.out = a->out; L.lse = a->lse;
+  L.ws = base + lay.attend; L.err = a->err;
+
+  if (a->mode == CSA_MODE_HCA) {
+    L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
+    L.a_stride = 0; L.vis_pos = a->pos; L.vis_ncomp = a->n_comp; L.vis_ratio = a->ratio;
+    L.kv_b = a->swa; L.b_rows = a->swa_rows; L.b_row0 = a->swa_row0; L.b_len = a->swa_len;
+    L.max_rows = (int)(a->max_vis + a->window);
+    return hip_status(launch_attend(L, st));
+  }
+
+  float* scores = a->scores ? a->scores : reinterpret_cast<float*>(base + lay.scores);
+  int32_t* idx = a->idx ? a->idx : reinterpret_cast<int32_t*>(base + lay.idx);
+  int32_t* count = a->count ? a->count : reinterpret_cast<int32_t*>(base + lay.count);
+  int32_t* n_kv = a->n_kv ? a->n_kv : reinterpret_cast<int32_t*>(base + lay.n_kv);
+  const TopkWs tw = topk_ws_carve(base + lay.topk, a->T, a->max_vis);
+  const int64_t nz = (reinterpret_cast<char*>(tw.cand) - reinterpret_cast<char*>(tw.hist)) / 4;
+
+  hipError_t e = launch_zero_u32(tw.hist, nz, st);
+  if (e == hipSuccess) {
+    IndexScoreLaunch I{a->q_idx, a->w, a->k_idx, a->k_rows, a->pos, a->seq_kv, a->n_comp, a->T,
+                       a->n_ih, a->ihd, a->ratio, scores, a->max_vis, tw.hist, a->err};
+    e = launch_index_score(I, st);
+  }
+  if (e == hipSuccess)
+    e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->T, a->ratio, a->top_k, idx,
+                           count, tw, a->err, st);
+  if (e == hipSuccess) {
+    GatherLaunch G{a->comp_kv, a->comp_rows, a->seq_kv, idx, count, a->top_k, a->swa,
+                   a->swa_rows, a->swa_row0, a->swa_len, a->window, a->T, a->head_dim,
+                   a->all_kv, n_kv, a->err};
+    e = launch_gather(G, st);
+  }
+  if (e == hipSuccess) {
+    L.kv_a = a->all_kv; L.a_rows = (int64_t)a->T * (a->top_k + a->window);
+    L.a_row0 = nullptr; L.a_len = n_kv; L.a_stride = a->top_k + a->window;
+    L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
+    L.kv_b = nullptr; L.b_rows = 0; L.b_row0 = nullptr; L.b_len = nullptr;
+    L.max_rows = a->top_k + a->window;
+    e = launch_attend(L, st);
+  }
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+"""libcsa on the host: it loads, exports every entry point that include/csa.h
+declares, and rejects bad arguments with the documented status before any
+GPU work (every call below fails validation or is a T == 0 no-op, so no
+kernel is launched and no device memory is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_long_context_index_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced here
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "csa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _header_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(b.EXPORTS)
+
+
+def test_status_strings_and_version(lib):
+    assert b.csa_abi_version() == 1
+    assert b.csa_status_str(0) == "CSA_OK"
+    for s in (1, 2, 3, 4):
+        assert b.csa_status_str(s).startswith("CSA_E")
+    assert "unknown" in b.csa_status_str(99)
+
+
+def _index(lib, **kw):
+    a = dict(q_idx=FAKE, w=FAKE, k_idx=FAKE, k_rows=100, pos=FAKE, seq_kv=FAKE, n_comp=FAKE,
+             T=1, n_ih=64, ihd=128, ratio=4, scores=FAKE, ld=100, err=None, stream=None)
+    a.update(kw)
+    return lib.csa_index_score(*a.values())
+
+
+def test_index_score_validation(lib):
+    assert _index(lib, T=0) == b.CSA_OK                      # no-op
+    assert _index(lib, q_idx=None) == b.CSA_EINVAL
+    assert _index(lib, scores=None) == b.CSA_EINVAL
+    assert _index(lib, ihd=48) == b.CSA_EUNSUPPORTED
+    assert _index(lib, n_ih=0) == b.CSA_EINVAL
+    assert _index(lib, n_ih=129) == b.CSA_EUNSUPPORTED
+    assert _index(lib, ratio=0) == b.CSA_EINVAL
+    assert _index(lib, ld=0) == b.CSA_EINVAL
+    assert _index(lib, T=-1) == b.CSA_EINVAL
+    assert _index(lib, q_idx=FAKE + 2) == b.CSA_EINVAL      # misaligned bf16 tensor
+    assert _index(lib, T=70000) == b.CSA_EUNSUPPORTED
+
+
+def test_topk_validation(lib):
+    args = lambda **kw: {**dict(scores=FAKE, ld=1000, pos=FAKE, n_comp=FAKE, T=1, ratio=4,  # noqa
+                                top_k=16, idx=FAKE, count=FAKE, ws=FAKE, ws_bytes=1 << 30,
+                                err=None, stream=None), **kw}
+    f = lambda **kw: lib.csa_topk(*args(**kw).values())  # noqa: E731
+    assert f(T=0) == b.CSA_OK
+    assert f(top_k=0) == b.CSA_EINVAL
+    assert f(top_k=2049) == b.CSA_EUNSUPPORTED
+    assert f(idx=None) == b.CSA_EINVAL
+    assert f(ws=None) == b.CSA_EWORKSPACE
+    assert f(ws=FAKE + 16) == b.CSA_EWORKSPACE               # not 256-byte aligned
+    need = b.csa_topk_workspace_bytes(1, 1000, 16)
+    assert need >= 1000 * 8
+    assert f(ws_bytes=need - 1) == b.CSA_EWORKSPACE
+
+
+def test_gather_validation(lib):
+    base = dict(comp_kv=FAKE, comp_rows=10, seq_kv=FAKE, idx=FAKE, count=FAKE, top_k=16,
+                swa=FAKE, swa_rows=16, swa_row0=FAKE, swa_len=FAKE, window=16, T=1,
+                head_dim=64, all_kv=FAKE, n_kv=FAKE, err=None, stream=None)
+    f = lambda **kw: lib.csa_gather(*{**base, **kw}.values())  # noqa: E731
+    assert f(T=0) == b.CSA_OK
+    assert f(head_dim=96) == b.CSA_EUNSUPPORTED
+    assert f(all_kv=None) == b.CSA_EINVAL
+    assert f(window=-1) == b.CSA_EINVAL
+    assert f(top_k=4096) == b.CSA_EUNSUPPORTED
+
+
+def test_attend_validation(lib):
+    base = dict(q=FAKE, T=1, n_heads=8, head_dim=64, scale=0.125, sink=None, kv_a=FAKE,
+                a_rows=100, a_row0=FAKE, a_len=FAKE, kv_b=None, b_rows=0, b_row0=None,
+                b_len=None, max_rows=100, out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30,
+                err=None, stream=None)
+    f = lambda **kw: lib.csa_mqa_attend(*{**base, **kw}.values())  # noqa: E731
+    assert f(T=0) == b.CSA_OK
+    assert f(head_dim=80) == b.CSA_EUNSUPPORTED
+    assert f(n_heads=0) == b.CSA_EINVAL
+    assert f(n_heads=129) == b.CSA_EUNSUPPORTED
+    assert f(kv_b=FAKE) == b.CSA_EINVAL                        # partial second segment
+    assert f(scale=float("nan")) == b.CSA_EINVAL
+    assert f(a_len=None) == b.CSA_EINVAL
+    big = b.csa_attend_workspace_bytes(1, 64, 512, 100000)
+    assert f(head_dim=512, n_heads=64, max_rows=100000, ws_bytes=big - 1) == b.CSA_EWORKSPACE
+
+
+def test_decode_step_validation(lib):
+    a = b.StepArgs()
+    a.mode, a.T, a.n_ih, a.ihd, a.ratio, a.top_k, a.window = 0, 1, 64, 128, 4, 1024, 128
+    a.n_heads, a.head_dim, a.max_vis, a.scale = 64, 512, 262144, 0.0441941738
+    for k in ("q_idx", "w", "k_idx", "comp_kv", "swa", "q", "pos", "seq_kv", "n_comp",
+              "swa_row0", "swa_len", "all_kv", "out"):
+        setattr(a, k, FAKE)
+    a.k_rows = a.comp_rows = 262144
+    a.swa_rows = 128
+    need = b.csa_decode_step_workspace_bytes(a)
+    # scores + candidate list dominate: 262,144 * (4 + 8) bytes plus small parts
+    assert need >= 262144 * 12
+    st = lambda ws, n: lib.csa_decode_step(ctypes.byref(a), ws, n, None)  # noqa: E731
+    assert st(None, 0) == b.CSA_EWORKSPACE
+    assert st(FAKE, need - 1) == b.CSA_EWORKSPACE
+    a.mode = 7
+    assert st(FAKE, need) == b.CSA_EINVAL
+    a.mode = 0
+    a.top_k = 0
+    assert st(FAKE, need) == b.CSA_EINVAL
+    a.top_k = 1024
+    a.all_kv = None
+    assert st(FAKE, need) == b.CSA_EINVAL
+    a.all_kv = FAKE
+    a.head_dim = 100
+    assert st(FAKE, need) == b.CSA_EUNSUPPORTED
+    a.head_dim = 512
+    a.T = 0
+    assert st(FAKE, need) == b.CSA_OK
+    assert lib.csa_decode_step(None, FAKE, need, None) == b.CSA_EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    t = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        b._p(t, (torch.float32,), "x")
