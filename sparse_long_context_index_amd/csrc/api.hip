@@ -91,7 +91,7 @@ StepWs step_ws_layout(const csa_step_args* a) {
     w.scores = off;
     if (!a->scores) off += align256((size_t)a->T * (size_t)a->max_vis * 4);
     w.topk = off;
-    off += topk_ws_bytes(a->T, a->max_vis);
+    off += topk_ws_layout(nullptr, a->T, plan_topk(a->T, a->max_vis, a->top_k)).bytes;
     w.idx = off;
     if (!a->idx) off += align256((size_t)a->T * a->top_k * 4);
     w.count = off;
@@ -134,6 +134,7 @@ csa_status check_step(const csa_step_args* a) {
       return CSA_EINVAL;
     if (a->ihd != 32 && a->ihd != 64 && a->ihd != 128) return CSA_EUNSUPPORTED;
     if (a->n_ih > 128 || a->top_k > kMaxTopk) return CSA_EUNSUPPORTED;
+    if (a->max_vis > INT32_MAX) return CSA_EUNSUPPORTED;
   }
   return CSA_OK;
 }
@@ -162,15 +163,17 @@ csa_status csa_index_score(const uint16_t* q_idx, const float* w, const uint16_t
   csa_status s = check_index(q_idx, w, k_idx, k_rows, pos, seq_kv, n_comp, T, n_ih, ihd, ratio,
                              scores, ld);
   if (s != CSA_OK || T == 0) return s;
-  IndexScoreLaunch L{q_idx, w, k_idx, k_rows, pos, seq_kv, n_comp, T, n_ih, ihd, ratio,
-                     scores, ld, nullptr, err};
+  IndexScoreLaunch L{};
+  L.q_idx = q_idx; L.w = w; L.k_idx = k_idx; L.k_rows = k_rows;
+  L.pos = pos; L.seq_kv = seq_kv; L.n_comp = n_comp;
+  L.T = T; L.n_ih = n_ih; L.ihd = ihd; L.ratio = ratio;
+  L.scores = scores; L.ld = ld; L.cand = nullptr; L.nvalid = nullptr; L.cand_m = 0; L.err = err;
   return hip_status(launch_index_score(L, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_topk_workspace_bytes(int T, int64_t ld, int top_k) {
-  (void)top_k;
-  if (T <= 0 || ld <= 0) return 0;
-  return topk_ws_bytes(T, ld);
+  if (T <= 0 || ld <= 0 || ld > INT32_MAX || top_k < 1) return 0;
+  return topk_ws_layout(nullptr, T, plan_topk(T, ld, top_k)).bytes;
 }
 
 csa_status csa_topk(const float* scores, int64_t ld, const int64_t* pos, const int32_t* n_comp,
@@ -178,15 +181,14 @@ csa_status csa_topk(const float* scores, int64_t ld, const int64_t* pos, const i
                     size_t ws_bytes, uint32_t* err, void* stream) {
   csa_status s = check_topk(scores, ld, pos, n_comp, T, ratio, top_k, idx, count);
   if (s != CSA_OK || T == 0) return s;
-  s = check_ws(ws, ws_bytes, topk_ws_bytes(T, ld));
+  const TopkPlan plan = plan_topk(T, ld, top_k);
+  s = check_ws(ws, ws_bytes, topk_ws_layout(nullptr, T, plan).bytes);
   if (s != CSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const TopkWs tw = topk_ws_carve(ws, T, ld);
-  const int64_t nz = (reinterpret_cast<char*>(tw.cand) - reinterpret_cast<char*>(tw.hist)) / 4;
-  hipError_t e = launch_zero_u32(tw.hist, nz, st);
-  if (e == hipSuccess) e = launch_score_hist(scores, ld, pos, n_comp, T, ratio, tw.hist, err, st);
+  const TopkWs tw = topk_ws_layout(ws, T, plan);
+  hipError_t e = launch_score_cands(scores, ld, pos, n_comp, T, ratio, plan, tw, err, st);
   if (e == hipSuccess)
-    e = launch_topk_select(scores, ld, pos, n_comp, T, ratio, top_k, idx, count, tw, err, st);
+    e = launch_topk_select(scores, ld, pos, n_comp, T, ratio, top_k, plan, tw, idx, count, err, st);
   return hip_status(e);
 }
 
@@ -198,8 +200,12 @@ csa_status csa_gather(const uint16_t* comp_kv, int64_t comp_rows, const int64_t*
   csa_status s = check_gather(comp_kv, comp_rows, seq_kv, idx, count, top_k, swa, swa_rows,
                               swa_row0, swa_len, window, T, head_dim, all_kv, n_kv);
   if (s != CSA_OK || T == 0) return s;
-  GatherLaunch L{comp_kv, comp_rows, seq_kv, idx, count, top_k, swa, swa_rows, swa_row0,
-                 swa_len, window, T, head_dim, all_kv, n_kv, err};
+  GatherLaunch L{};
+  L.comp_kv = comp_kv; L.comp_rows = comp_rows; L.seq_kv = seq_kv;
+  L.idx = idx; L.count = count; L.top_k = top_k;
+  L.swa = swa; L.swa_rows = swa_rows; L.swa_row0 = swa_row0; L.swa_len = swa_len;
+  L.window = window; L.T = T; L.head_dim = head_dim;
+  L.all_kv = all_kv; L.n_kv = n_kv; L.err = err;
   return hip_status(launch_gather(L, static_cast<hipStream_t>(stream)));
 }
 
@@ -262,29 +268,27 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   int32_t* idx = a->idx ? a->idx : reinterpret_cast<int32_t*>(base + lay.idx);
   int32_t* count = a->count ? a->count : reinterpret_cast<int32_t*>(base + lay.count);
   int32_t* n_kv = a->n_kv ? a->n_kv : reinterpret_cast<int32_t*>(base + lay.n_kv);
-  const TopkWs tw = topk_ws_carve(base + lay.topk, a->T, a->max_vis);
-  const int64_t nz = (reinterpret_cast<char*>(tw.cand) - reinterpret_cast<char*>(tw.hist)) / 4;
+  const TopkPlan tp = plan_topk(a->T, a->max_vis, a->top_k);
+  const TopkWs tw = topk_ws_layout(base + lay.topk, a->T, tp);
 
-  hipError_t e = launch_zero_u32(tw.hist, nz, st);
-  if (e == hipSuccess) {
-    IndexScoreLaunch I{a->q_idx, a->w, a->k_idx, a->k_rows, a->pos, a->seq_kv, a->n_comp, a->T,
-                       a->n_ih, a->ihd, a->ratio, scores, a->max_vis, tw.hist, a->err};
-    e = launch_index_score(I, st);
-  }
+  // S1 (+ per-wave candidate lists) -> S2 -> S3 fused into S4.
+  IndexScoreLaunch I{};
+  I.q_idx = a->q_idx; I.w = a->w; I.k_idx = a->k_idx; I.k_rows = a->k_rows;
+  I.pos = a->pos; I.seq_kv = a->seq_kv; I.n_comp = a->n_comp;
+  I.T = a->T; I.n_ih = a->n_ih; I.ihd = a->ihd; I.ratio = a->ratio;
+  I.scores = scores; I.ld = a->max_vis;
+  I.cand = tw.cand; I.nvalid = tw.nvalid; I.cand_m = tp.cand_m; I.err = a->err;
+  hipError_t e = launch_index_score(I, st);
   if (e == hipSuccess)
-    e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->T, a->ratio, a->top_k, idx,
-                           count, tw, a->err, st);
+    e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->T, a->ratio, a->top_k, tp,
+                           tw, idx, count, a->err, st);
   if (e == hipSuccess) {
-    GatherLaunch G{a->comp_kv, a->comp_rows, a->seq_kv, idx, count, a->top_k, a->swa,
-                   a->swa_rows, a->swa_row0, a->swa_len, a->window, a->T, a->head_dim,
-                   a->all_kv, n_kv, a->err};
-    e = launch_gather(G, st);
-  }
-  if (e == hipSuccess) {
-    L.kv_a = a->all_kv; L.a_rows = (int64_t)a->T * (a->top_k + a->window);
-    L.a_row0 = nullptr; L.a_len = n_kv; L.a_stride = a->top_k + a->window;
-    L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
-    L.kv_b = nullptr; L.b_rows = 0; L.b_row0 = nullptr; L.b_len = nullptr;
+    L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
+    L.a_stride = 0; L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
+    L.sel_idx = idx; L.sel_cnt = count; L.sel_stride = a->top_k;
+    L.kv_b = a->swa; L.b_rows = a->swa_rows; L.b_row0 = a->swa_row0; L.b_len = a->swa_len;
+    L.b_cap = a->window;
+    L.copy_out = a->all_kv; L.copy_stride = a->top_k + a->window; L.n_kv_out = n_kv;
     L.max_rows = a->top_k + a->window;
     e = launch_attend(L, st);
   }

@@ -18,7 +18,10 @@
 //     combine kernel merges them (and applies the sink).  With one split the
 //     workgroup writes the final output directly.
 // The row set of token t is segment A followed by segment B, read in place, so
-// the HCA path needs no concatenation and the CSA path reads all_kv.
+// the HCA path needs no concatenation.  In the decode step the CSA rows are
+// gathered here (selected compressed rows through their block indices, then
+// the SWA rows) and copied into all_kv while they are staged, which fuses the
+// gather stage into the attention.
 #include "csa_common.h"
 
 namespace csa {
@@ -26,6 +29,8 @@ namespace {
 
 constexpr int kRT = 64;          // rows per tile
 constexpr int kHeadsPerWg = 64;  // 4 waves x 16 heads
+constexpr int kMaxSplits = 256;
+constexpr int64_t kSegB = 1ll << 62;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -44,24 +49,40 @@ struct SegDesc {
   int alen, blen;
 };
 
+// Row set of token t.  Gather mode (p.sel_idx != nullptr): segment A is the
+// selected compressed rows comp_kv[seq_kv[t] + sel_idx[t, j]], j < sel_cnt[t],
+// segment B the SWA rows; the rows are also copied into all_kv while staged.
 __device__ SegDesc token_rows(const AttendLaunch& p, int t, uint32_t& flags) {
   SegDesc s;
-  s.a0 = p.a_row0 != nullptr ? p.a_row0[t] : (int64_t)t * p.a_stride;
   int64_t alen;
-  if (p.vis_pos != nullptr) {
-    alen = visible_count(p.vis_pos[t], p.vis_ratio, p.vis_ncomp[t], &flags);
+  if (p.sel_idx != nullptr) {
+    s.a0 = p.a_row0[t];  // seq_kv
+    alen = p.sel_cnt[t];
+    if (alen < 0 || alen > p.sel_stride) {
+      flags |= CSA_DERR_COUNT_RANGE;
+      alen = alen < 0 ? 0 : p.sel_stride;
+    }
   } else {
-    alen = p.a_len[t];
-  }
-  if (s.a0 < 0 || alen < 0 || s.a0 + alen > p.a_rows) {
-    flags |= CSA_DERR_ROW_RANGE;
-    alen = 0;
+    s.a0 = p.a_row0 != nullptr ? p.a_row0[t] : (int64_t)t * p.a_stride;
+    if (p.vis_pos != nullptr) {
+      alen = visible_count(p.vis_pos[t], p.vis_ratio, p.vis_ncomp[t], &flags);
+    } else {
+      alen = p.a_len[t];
+    }
+    if (s.a0 < 0 || alen < 0 || s.a0 + alen > p.a_rows) {
+      flags |= CSA_DERR_ROW_RANGE;
+      alen = 0;
+    }
   }
   int64_t blen = 0;
   s.b0 = 0;
   if (p.kv_b != nullptr) {
     s.b0 = p.b_row0[t];
     blen = p.b_len[t];
+    if (p.sel_idx != nullptr && blen > p.b_cap) {
+      flags |= CSA_DERR_COUNT_RANGE;
+      blen = p.b_cap;
+    }
     if (s.b0 < 0 || blen < 0 || s.b0 + blen > p.b_rows) {
       flags |= CSA_DERR_ROW_RANGE;
       blen = 0;
@@ -91,6 +112,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   __shared__ __attribute__((aligned(16))) uint16_t rm[L::RM_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t il[L::IL_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t pb[L::P_ELEMS];
+  __shared__ int64_t rsrc[kRT];  // element offset of each tile row (kSegB: segment B), -1: none
 
   const int t = blockIdx.z;
   const int split = blockIdx.x;
@@ -99,11 +121,20 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int li = lane & 15, quad = lane >> 4;
   const int h0 = blockIdx.y * kHeadsPerWg + wave * 16;
 
+  // selected block indices of the first tile, loaded before anything they
+  // would wait on (idx rows always hold sel_stride entries)
+  int32_t pidx = 0;
+  const int row_begin = split * tiles_per_split * kRT;
+  if (p.sel_idx != nullptr && tid < kRT)
+    pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(row_begin + tid, p.sel_stride - 1)];
   uint32_t flags = 0;
   const SegDesc sd = token_rows(p, t, flags);
-  if (split == 0 && blockIdx.y == 0 && tid == 0) report(p.err, flags);
+  if (split == 0 && blockIdx.y == 0 && tid == 0) {
+    report(p.err, flags);
+    if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
+  }
+  flags = 0;
   const int n_rows = sd.alen + sd.blen;
-  const int row_begin = split * tiles_per_split * kRT;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
 
   // Q (A operand): lane holds head h0+li, d = ks*32 + quad*8 .. +8.
@@ -134,31 +165,68 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const uint16_t* kv_b = p.kv_b;
   for (int r0 = row_begin; r0 < row_end; r0 += kRT) {
     __syncthreads();  // the previous tile has been consumed
-    // ---- stage the tile: 8x8 (rows x d) blocks, one per thread per pass ----
-    for (int b = tid; b < (kRT / 8) * DP; b += 256) {
+    // ---- row sources of this tile: one thread per row resolves the block
+    // index (gather mode) or segment B, into an LDS table ----
+    if (tid < kRT) {
+      const int rr = r0 + tid;
+      int64_t o = -1;
+      if (rr < row_end) {
+        if (rr < sd.alen) {
+          int64_t ar = sd.a0 + rr;
+          if (p.sel_idx != nullptr) {
+            ar = sd.a0 + pidx;
+            if (ar < 0 || ar >= p.a_rows) {
+              flags |= CSA_DERR_ROW_RANGE;
+              ar = -1;
+            }
+          }
+          o = ar < 0 ? -1 : ar * D;
+        } else {
+          o = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
+        }
+      }
+      rsrc[tid] = o;
+      // prefetch the next tile's block indices
+      if (p.sel_idx != nullptr && r0 + kRT < row_end)
+        pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(r0 + kRT + tid, p.sel_stride - 1)];
+    }
+    __syncthreads();
+    // ---- stage the tile: 8x8 (rows x d) blocks; all loads issued first ----
+    constexpr int NB = (kRT / 8) * DP;             // 8x8 blocks per tile
+    constexpr int BPTH = (NB + 255) / 256;         // blocks per thread
+    u32x4 rows[BPTH][8];
+#pragma unroll
+    for (int q = 0; q < BPTH; ++q) {
+      const int b = tid + q * 256;
       const int g = b / DP, dp = b - g * DP;
-      u32x4 rows[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int rr = r0 + g * 8 + k;
-        rows[k] = u32x4{0u, 0u, 0u, 0u};
-        if (rr < row_end) {
-          const uint16_t* src = rr < sd.alen ? kv_a + (sd.a0 + rr) * D
-                                             : kv_b + (sd.b0 + (rr - sd.alen)) * D;
-          rows[k] = *reinterpret_cast<const u32x4*>(src + dp * 8);
+        const int64_t o = b < NB ? rsrc[g * 8 + k] : -1;
+        rows[q][k] = u32x4{0u, 0u, 0u, 0u};
+        if (o >= 0) {
+          const uint16_t* base = (o & kSegB) ? kv_b : kv_a;
+          rows[q][k] = *reinterpret_cast<const u32x4*>(base + (o & ~kSegB) + dp * 8);
         }
-        *reinterpret_cast<u32x4*>(&rm[(g * 8 + k) * L::RM + dp * 8]) = rows[k];
       }
+    }
+#pragma unroll
+    for (int q = 0; q < BPTH; ++q) {
+      const int b = tid + q * 256;
+      if (b >= NB) break;
+      const int g = b / DP, dp = b - g * DP;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<u32x4*>(&rm[(g * 8 + k) * L::RM + dp * 8]) = rows[q][k];
       uint16_t* ilg = &il[g * L::ILG + dp * 8 * 8 + dp * 8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const int wi = e >> 1;
         u32x4 c;
-        c.x = perm(rows[1][wi], rows[0][wi], sel);
-        c.y = perm(rows[3][wi], rows[2][wi], sel);
-        c.z = perm(rows[5][wi], rows[4][wi], sel);
-        c.w = perm(rows[7][wi], rows[6][wi], sel);
+        c.x = perm(rows[q][1][wi], rows[q][0][wi], sel);
+        c.y = perm(rows[q][3][wi], rows[q][2][wi], sel);
+        c.z = perm(rows[q][5][wi], rows[q][4][wi], sel);
+        c.w = perm(rows[q][7][wi], rows[q][6][wi], sel);
         *reinterpret_cast<u32x4*>(ilg + e * 8) = c;
       }
     }
@@ -241,8 +309,19 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[n], 0, 0, 0);
       }
     }
+    // gather mode: copy the staged rows to all_kv (off the staging critical path)
+    if (p.copy_out != nullptr) {
+      for (int c = tid; c < kRT * DP; c += 256) {
+        const int r = c / DP, dp = c - r * DP;
+        const int rr = r0 + r;
+        if (rr < row_end)
+          *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + rr) * D + dp * 8) =
+              *reinterpret_cast<const u32x4*>(&rm[r * L::RM + dp * 8]);
+      }
+    }
   }
 
+  report(p.err, flags);
   // ---- epilogue: o[n][r] = O[head 4*quad + r][d = n*16 + li] ----
   if (n_splits == 1) {
 #pragma unroll
@@ -285,38 +364,76 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   }
 }
 
+// Merge of the split partials of one (token, head): all split weights are
+// formed at once (one split per lane), then the partial rows are accumulated
+// with their loads batched four splits at a time.
 template <int D>
 __global__ __launch_bounds__(64) void attend_combine_kernel(AttendLaunch p, int n_splits) {
   constexpr int EPL = D / 64;
+  __shared__ float fw[kMaxSplits];
   const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
   const float* part_o = static_cast<const float*>(p.ws);
   const float* part_ml = part_o + (size_t)p.T * n_splits * p.n_heads * D;
   const size_t slot0 = (size_t)t * n_splits * p.n_heads + h;
+  constexpr int SPL = kMaxSplits / 64;
+  float m[SPL], l[SPL];
   float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) {
-    const size_t slot = slot0 + (size_t)s * p.n_heads;
-    if (part_ml[slot * 2 + 1] > 0.f) M = fmaxf(M, part_ml[slot * 2]);
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int s = lane + 64 * i;
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+    if (s < n_splits) {
+      const size_t slot = slot0 + (size_t)s * p.n_heads;
+      m[i] = part_ml[slot * 2];
+      l[i] = part_ml[slot * 2 + 1];
+      if (l[i] > 0.f) M = fmaxf(M, m[i]);
+    }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float s2 = -INFINITY;
   if (p.sink != nullptr) {
     s2 = p.sink[h] * kLog2e;
     M = fmaxf(M, s2);
   }
+  float Lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int s = lane + 64 * i;
+    const float f = (l[i] > 0.f) ? exp2f(m[i] - M) : 0.f;
+    Lsum += l[i] * f;
+    if (s < n_splits) fw[s] = f;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Lsum += __shfl_xor(Lsum, off);
+  if (p.sink != nullptr) Lsum += exp2f(s2 - M);
+  __syncthreads();
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  float Lsum = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const size_t slot = slot0 + (size_t)s * p.n_heads;
-    const float l = part_ml[slot * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float f = exp2f(part_ml[slot * 2] - M);
-    Lsum += l * f;
-    const float* po = part_o + slot * D + lane * EPL;
+  const float* pb = part_o + slot0 * D + lane * EPL;
+  const size_t sstride = (size_t)p.n_heads * D;
+  for (int s0 = 0; s0 < n_splits; s0 += 4) {
+    float v[4][EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[j] += f * po[j];
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[u][j] = 0.f;
+      if (s < n_splits && fw[s] != 0.f) {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) v[u][j] = pb[(size_t)s * sstride + j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u;
+      const float f = s < n_splits ? fw[s] : 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) acc[j] += f * v[u][j];
+    }
   }
-  if (p.sink != nullptr) Lsum += exp2f(s2 - M);
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   uint16_t* oh = p.out + ((size_t)t * p.n_heads + h) * D + lane * EPL;
 #pragma unroll
@@ -336,6 +453,7 @@ SplitPlan plan_splits(int T, int n_heads, int max_rows) {
   int want = (256 + T * n_hg - 1) / (T * n_hg);
   if (want < 1) want = 1;
   if (want > n_tiles) want = n_tiles;
+  if (want > kMaxSplits) want = kMaxSplits;
   sp.tiles_per_split = (n_tiles + want - 1) / want;
   sp.n_splits = (n_tiles + sp.tiles_per_split - 1) / sp.tiles_per_split;
   return sp;

@@ -26,9 +26,40 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Number of top key bits histogrammed by the first (multi-workgroup) pass.
-constexpr int kHistBits = 11;
-constexpr int kHistBins = 1 << kHistBits;
+// Composite selection key of block s with score f: the score key in the high
+// word, the complemented block index in the low word.  Unique per block;
+// larger score first, then lower block index.  Zero marks an empty slot.
+__device__ __forceinline__ uint64_t block_key(float f, uint32_t s) {
+  return ((uint64_t)score_key(f) << 32) | (uint32_t)(~s);
+}
+
+// Wave-level top-m of composite keys held by the lanes (KPL per lane, zero =
+// empty): the m largest keys, descending, zero-padded, are written by lane 0
+// to out[0..m).  The keys are consumed.
+template <int KPL>
+__device__ __forceinline__ void wave_top_m(uint64_t (&key)[KPL], int m, uint64_t* out) {
+  const int lane = threadIdx.x & 63;
+  for (int i = 0; i < m; ++i) {
+    uint64_t lm = 0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) lm = key[q] > lm ? key[q] : lm;
+    uint64_t wm = lm;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t o = __shfl_xor((unsigned long long)wm, off);
+      wm = o > wm ? o : wm;
+    }
+    if (lane == 0) out[i] = wm;
+    if (wm == 0) {  // wave-uniform
+      if (lane == 0)
+        for (int r = i + 1; r < m; ++r) out[r] = 0;
+      break;
+    }
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+      if (key[q] == wm) key[q] = 0;
+  }
+}
 
 // Visible-block count of a token; flags inconsistent metadata.  Mirrors the
 // causal rule: blocks strictly before the query's own block, capped by the
@@ -71,27 +102,41 @@ struct IndexScoreLaunch {
   const int64_t* pos; const int64_t* seq_kv; const int32_t* n_comp;
   int T, n_ih, ihd, ratio;
   float* scores; int64_t ld;
-  uint32_t* hist;   // [T, kHistBins] or nullptr: fused top-bits histogram
+  uint64_t* cand;   // [T, waves_per_token, cand_m] or nullptr: per-wave top-m keys
+  uint32_t* nvalid; // [T, waves_per_token] valid blocks of each wave
+  int cand_m;
   uint32_t* err;
 };
+constexpr int kIndexWaves = 4;  // waves per indexer workgroup
+struct IndexPlan {
+  int tiles_per_wave, wgs_per_token;
+  int waves_per_token() const { return wgs_per_token * kIndexWaves; }
+  int blocks_per_wave() const { return 32 * tiles_per_wave; }
+};
+IndexPlan plan_index(int T, int64_t ld);
 hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s);
 
-// Top-k workspace, per token: hist[kHistBins] u32, ctr[4] u32, cand[ld] u64.
-struct TopkWs {
-  uint32_t* hist;    // [T, kHistBins]
-  uint32_t* ctr;     // [T, 4]: above count, candidate count, ticket, spare
-  uint64_t* cand;    // [T, ld]
+// Top-k (see topk.hip).  Candidate layout shared with the indexer epilogue.
+constexpr int kPoolCap = 12288;  // keys the select workgroup holds in LDS
+struct TopkPlan {
+  int waves_per_token;   // candidate lists per token
+  int blocks_per_wave;   // blocks behind each list
+  int cand_m;            // keys per list (0: every token selects from its scores directly)
 };
-size_t topk_ws_bytes(int T, int64_t ld);
-TopkWs topk_ws_carve(void* ws, int T, int64_t ld);
-hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
-hipError_t launch_score_hist(const float* scores, int64_t ld, const int64_t* pos,
-                             const int32_t* n_comp, int T, int ratio, uint32_t* hist,
-                             uint32_t* err, hipStream_t s);
+TopkPlan plan_topk(int T, int64_t ld, int top_k);
+struct TopkWs {
+  uint64_t* cand;    // [T, waves_per_token, cand_m]
+  uint32_t* nvalid;  // [T, waves_per_token]
+  size_t bytes;
+};
+TopkWs topk_ws_layout(void* ws, int T, const TopkPlan& p);
+hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* pos,
+                              const int32_t* n_comp, int T, int ratio, const TopkPlan& p,
+                              const TopkWs& ws, uint32_t* err, hipStream_t s);
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int64_t* pos,
                               const int32_t* n_comp, int T, int ratio, int top_k,
-                              int32_t* idx, int32_t* count, const TopkWs& ws,
-                              uint32_t* err, hipStream_t s);
+                              const TopkPlan& p, const TopkWs& ws, int32_t* idx,
+                              int32_t* count, uint32_t* err, hipStream_t s);
 
 struct GatherLaunch {
   const uint16_t* comp_kv; int64_t comp_rows; const int64_t* seq_kv;
@@ -102,16 +147,21 @@ struct GatherLaunch {
 };
 hipError_t launch_gather(const GatherLaunch& a, hipStream_t s);
 
-// Segment A of the attention row set is described either explicitly
-// (row0/len arrays) or, for the HCA path, derived from the visibility rule
-// (row0 = seq_kv[t], len = n_vis[t]); or, for the CSA path, as token t's slice
-// of all_kv (row0 = t*a_stride, len = n_kv[t]).
+// Row set of each token: segment A then segment B.  Segment A is one of
+//   * explicit: rows a_row0[t] .. +a_len[t] of kv_a;
+//   * visibility (HCA): rows a_row0[t] .. +n_vis[t] (vis_pos != nullptr);
+//   * gather (CSA decode step, sel_idx != nullptr): rows a_row0[t] + sel_idx[t, j]
+//     for j < sel_cnt[t], also copied to copy_out[t, j] with the SWA rows after
+//     them, and n_kv_out[t] = rows used.
 struct AttendLaunch {
   const uint16_t* q; int T, n_heads, head_dim; float scale; const float* sink;
   const uint16_t* kv_a; int64_t a_rows; const int64_t* a_row0; const int32_t* a_len;
-  int64_t a_stride;                       // >0: row0 = t*a_stride (a_row0 unused)
-  const int64_t* vis_pos; const int32_t* vis_ncomp; int vis_ratio;  // HCA: len = n_vis
+  int64_t a_stride;                       // a_row0 == nullptr: row0 = t*a_stride
+  const int64_t* vis_pos; const int32_t* vis_ncomp; int vis_ratio;
+  const int32_t* sel_idx; const int32_t* sel_cnt; int sel_stride;
   const uint16_t* kv_b; int64_t b_rows; const int64_t* b_row0; const int32_t* b_len;
+  int b_cap;                              // gather mode: at most this many B rows
+  uint16_t* copy_out; int64_t copy_stride; int32_t* n_kv_out;
   int max_rows;
   uint16_t* out; float* lse;
   void* ws; uint32_t* err;

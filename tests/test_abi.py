@@ -63,7 +63,9 @@ def test_index_score_validation(lib):
 
 
 def test_topk_validation(lib):
-    args = lambda **kw: {**dict(scores=FAKE, ld=1000, pos=FAKE, n_comp=FAKE, T=1, ratio=4,  # noqa
+    # a row longer than the LDS pool needs candidate lists in the workspace
+    ld = 100000
+    args = lambda **kw: {**dict(scores=FAKE, ld=ld, pos=FAKE, n_comp=FAKE, T=1, ratio=4,  # noqa
                                 top_k=16, idx=FAKE, count=FAKE, ws=FAKE, ws_bytes=1 << 30,
                                 err=None, stream=None), **kw}
     f = lambda **kw: lib.csa_topk(*args(**kw).values())  # noqa: E731
@@ -73,9 +75,11 @@ def test_topk_validation(lib):
     assert f(idx=None) == b.CSA_EINVAL
     assert f(ws=None) == b.CSA_EWORKSPACE
     assert f(ws=FAKE + 16) == b.CSA_EWORKSPACE               # not 256-byte aligned
-    need = b.csa_topk_workspace_bytes(1, 1000, 16)
-    assert need >= 1000 * 8
+    need = b.csa_topk_workspace_bytes(1, ld, 16)
+    assert need > 0
     assert f(ws_bytes=need - 1) == b.CSA_EWORKSPACE
+    # rows that fit the LDS pool select straight from the scores: no workspace
+    assert b.csa_topk_workspace_bytes(4, 12288, 1024) == 0
 
 
 def test_gather_validation(lib):
@@ -117,8 +121,8 @@ def test_decode_step_validation(lib):
     a.k_rows = a.comp_rows = 262144
     a.swa_rows = 128
     need = b.csa_decode_step_workspace_bytes(a)
-    # scores + candidate list dominate: 262,144 * (4 + 8) bytes plus small parts
-    assert need >= 262144 * 12
+    # at least the scores of 262,144 blocks plus the attention split partials
+    assert need >= 262144 * 4 + 64 * 512 * 4
     st = lambda ws, n: lib.csa_decode_step(ctypes.byref(a), ws, n, None)  # noqa: E731
     assert st(None, 0) == b.CSA_EWORKSPACE
     assert st(FAKE, need - 1) == b.CSA_EWORKSPACE

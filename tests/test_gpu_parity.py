@@ -153,6 +153,29 @@ def test_topk_many_candidates_global_path(dev):
     _topk_case(dev, [x], 1000, "one-bin")
 
 
+def test_topk_clustered_top_blocks(dev):
+    """The 1024 best blocks are contiguous: the groups holding them list only
+    their top few keys, so they must be re-scanned in full."""
+    r = np.random.default_rng(15)
+    x = r.standard_normal(262144).astype(np.float32)
+    x[70001:71025] = 10.0 + r.random(1024).astype(np.float32)
+    _topk_case(dev, [x], 1024, "clustered")
+
+
+def test_topk_spread_groups_global_path(dev):
+    """Four top scores in each of 256 groups: too many groups to re-scan in
+    the LDS pool, so the select falls back to the scores in global memory."""
+    r = np.random.default_rng(16)
+    x = (r.standard_normal(262144) * 0.1).astype(np.float32)
+    for g in range(256):
+        x[g * 1024 + np.arange(4) * 7] = 5.0 + r.random(4).astype(np.float32)
+    _topk_case(dev, [x], 1024, "spread")
+
+
+def test_topk_all_equal_long_row(dev):
+    _topk_case(dev, [np.full(300000, 0.5, dtype=np.float32)], 1024, "equal-300k")
+
+
 def test_topk_1m_sized(dev):
     r = np.random.default_rng(14)
     _topk_case(dev, [(r.standard_normal(262144) * 8 + 3).astype(np.float32)], 1024, "262144")
