@@ -6,35 +6,92 @@
 // score first, then lower block index, so the selected set is exactly the
 // k_eff largest keys and ties at the k-th score go to the lower index.
 //
-// One workgroup per token selects, in LDS, from a pool of keys:
-//   * n_vis <= kPoolCap: the pool is every visible block (exact, direct);
-//   * otherwise the pool is the candidate lists -- the top-m keys of every
+// One 1024-thread workgroup per token selects from a key set held in
+// registers (12 keys per thread) plus an LDS overflow area:
+//   * n_vis <= kPoolCap: the keys are every visible block (exact, direct);
+//   * otherwise the keys are the candidate lists -- the top-m keys of every
 //     group of blocks handled by one indexer wave, written by the indexer
-//     epilogue (or score_cands_kernel).  Let T1 be the k_eff-th largest pool
-//     key.  A group whose list is full (it has more than m blocks) and whose
-//     m-th key is >= T1 may hold unlisted blocks above T1; all its blocks are
-//     added to the pool and the selection is repeated.  Every other unlisted
-//     block is below its group's m-th key < T1, below k_eff pool keys, so the
-//     result is exact.  At most k_eff/m groups can qualify (each puts m keys
-//     >= T1 into the pool, and only k_eff pool keys are >= T1), which bounds
-//     the extra work;
-//   * if the pool would not fit, the select runs over the token's scores in
-//     global memory (slow, exact; only for adversarial score layouts).
-// The threshold is found by 8-bit radix passes over the 64-bit keys with a
-// block-wide bin search; the selection is written in ascending block order
-// by scanning an LDS bitmap of the visible range.
+//     epilogue (or score_cands_kernel).  Let T1 be the k_eff-th largest
+//     listed key.  A group whose list is full (it has more than m blocks) and
+//     whose m-th key is >= T1 may hold unlisted blocks above T1; its unlisted
+//     blocks are added and the threshold is found again.  Every other
+//     unlisted block is below its group's m-th key < T1, below k_eff listed
+//     keys, so the result is exact.  At most k_eff/m groups can qualify (each
+//     puts m keys >= T1 into the set, and only k_eff keys are >= T1);
+//   * if the extra blocks would not fit, the select runs over the token's
+//     scores in global memory (slow, exact; only for adversarial layouts).
 //
-// No global atomics: on this chip same-address device-scope atomics serialise
-// at ~12 ns each, so cross-workgroup communication is plain stores plus the
+// The k-th key is found in one histogram pass over 2048 bins laid linearly
+// over [min, max] of the scores (a monotone map, so bins are ordered), then an
+// exact rank among the few keys of the threshold bin.  Linear bins spread the
+// keys, which keeps LDS atomics free of same-address conflicts; where the
+// threshold bin is crowded (ties, clustered values) an exact 8-bit radix
+// select over the composite keys takes over.  The selection is written in
+// ascending block order by scanning an LDS bitmap of the visible range.
+//
+// No global atomics: cross-workgroup communication is plain stores plus the
 // kernel boundary.
+#include <math.h>
+
 #include "csa_common.h"
 
 namespace csa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBitmapWords = 8192;  // 262,144 blocks per emission sweep
-constexpr int kMaxOv = 512;         // groups re-scanned in full before falling back
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int KPT = kPoolCap / kThreads;  // register keys per thread
+constexpr int kBins = 2 * kThreads;       // linear bins, two per thread
+constexpr int kXCap = 4096;               // keys of re-scanned groups (LDS)
+constexpr int kListCap = 1024;            // threshold-bin keys ranked exactly
+constexpr int kMaxOv = 512;               // groups re-scanned before falling back
+constexpr int kBitmapWords = 8192;        // 262,144 blocks per emission sweep
+static_assert(KPT * kThreads == kPoolCap, "pool must split evenly");
+static_assert(kBitmapWords % (8 * kThreads) == 0, "8 bitmap words per thread");
+
+struct SelShared {
+  uint32_t bitmap[kBitmapWords];
+  uint64_t xk[kXCap];
+  uint64_t list[kListCap];
+  uint32_t hist[kBins];
+  uint32_t ov_w[kMaxOv];
+  uint32_t ov_nv[kMaxOv];
+  uint64_t ov_cut[kMaxOv];
+  uint32_t scratch[2 * kWaves + 8];
+  uint64_t red64[2 * kWaves];
+  float redf[2 * kWaves];
+  uint64_t thr;
+  uint32_t n_x, n_ov, n_list;
+};
+
+// Score of a composite key (inverse of score_key on the high word).
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Linear bin of a key's score: non-decreasing in the key for s > 0 (the
+// subtraction, product, clamp and truncation are all monotone).
+__device__ __forceinline__ uint32_t key_bin(uint64_t key, float lo, float s) {
+  const float x = (key_value(key) - lo) * s;
+  return (uint32_t)fminf(fmaxf(x, 0.0f), (float)(kBins - 1));
+}
+
+// Appends v (where p) to list[0..cap) at *n; one LDS atomic per wave.
+__device__ __forceinline__ void wave_append(bool p, uint64_t v, uint64_t* list, uint32_t* n,
+                                            uint32_t cap) {
+  const uint64_t mask = __ballot(p);
+  if (mask == 0ull) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(mask));
+  base = __shfl(base, leader);
+  if (p) {
+    const uint32_t o = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+    if (o < cap) list[o] = v;
+  }
+}
 
 // Block-wide search in a histogram distributed over the workgroup: thread i
 // owns bins [i*BPT, i*BPT+BPT) in `c`.  Finds the bin b with
@@ -42,7 +99,8 @@ constexpr int kMaxOv = 512;         // groups re-scanned in full before falling 
 // and returns b and the count above it.  Requires 1 <= need <= total.
 template <int BPT>
 __device__ __forceinline__ void find_threshold_bin(const uint32_t (&c)[BPT], uint32_t need,
-                                   uint32_t* scratch, uint32_t& bin, uint32_t& above) {
+                                                   uint32_t* scratch, uint32_t& bin,
+                                                   uint32_t& above) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t tot = 0;
 #pragma unroll
@@ -56,23 +114,24 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t (&c)[BPT], uin
   if (lane == 0) scratch[wave] = x;
   __syncthreads();
   uint32_t acc = x - tot;
-  for (int wv = wave + 1; wv < kThreads / 64; ++wv) acc += scratch[wv];
+  for (int wv = wave + 1; wv < kWaves; ++wv) acc += scratch[wv];
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
     if (acc < need && acc + c[i] >= need) {
-      scratch[4] = (uint32_t)(tid * BPT + i);
-      scratch[5] = acc;
+      scratch[kWaves] = (uint32_t)(tid * BPT + i);
+      scratch[kWaves + 1] = acc;
     }
     acc += c[i];
   }
   __syncthreads();
-  bin = scratch[4];
-  above = scratch[5];
+  bin = scratch[kWaves];
+  above = scratch[kWaves + 1];
   __syncthreads();
 }
 
 // Exclusive prefix sum over the workgroup (ascending thread order).
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch,
+                                                    uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -84,7 +143,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   __syncthreads();
   uint32_t base = 0;
   total = 0;
-  for (int wv = 0; wv < kThreads / 64; ++wv) {
+  for (int wv = 0; wv < kWaves; ++wv) {
     if (wv < wave) base += scratch[wv];
     total += scratch[wv];
   }
@@ -92,28 +151,42 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   return base + x - v;
 }
 
-__device__ __forceinline__ int64_t token_visible(const int64_t* pos, const int32_t* n_comp,
-                                                 int t, int ratio, int64_t ld) {
-  uint32_t f = 0;
-  int64_t n_vis = visible_count(pos[t], ratio, n_comp[t], &f);
-  return n_vis > ld ? ld : n_vis;
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
+  uint32_t total;
+  block_excl_scan(v, scratch, total);
+  return total;
 }
 
-struct SelShared {
-  uint64_t pool[kPoolCap];
-  uint32_t bitmap[kBitmapWords + kBitmapWords / 32];  // word w at w + w/32 (bank padding)
-  uint32_t dh4[kThreads / 64][256];                    // per-wave digit histograms
-  uint32_t dh[256];
-  uint32_t scratch[16];
-  uint32_t ov_w[kMaxOv];
-  uint32_t ov_off[kMaxOv + 1];
-  uint64_t ov_cut[kMaxOv];
-  uint64_t red[8];
-  uint32_t n_pool, n_ov;
-};
+// Block-wide count, min and max (of the scores) of the nonzero keys.
+__device__ __forceinline__ void block_count_range(uint32_t n, float lo, float hi, SelShared& sh,
+                                                  uint32_t& bn, float& blo, float& bhi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    n += __shfl_xor(n, off);
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  if (lane == 0) {
+    sh.scratch[wave] = n;
+    sh.redf[wave] = lo;
+    sh.redf[kWaves + wave] = hi;
+  }
+  __syncthreads();
+  bn = 0;
+  blo = INFINITY;
+  bhi = -INFINITY;
+  for (int w = 0; w < kWaves; ++w) {
+    bn += sh.scratch[w];
+    blo = fminf(blo, sh.redf[w]);
+    bhi = fmaxf(bhi, sh.redf[kWaves + w]);
+  }
+  __syncthreads();
+}
 
-// Block-wide max, and min over nonzero values, of 64-bit keys.
-__device__ __forceinline__ void block_minmax(uint64_t lo, uint64_t hi, SelShared& sh, uint64_t& blo, uint64_t& bhi) {
+// Block-wide min over nonzero keys and max of 64-bit keys.
+__device__ __forceinline__ void block_minmax64(uint64_t lo, uint64_t hi, SelShared& sh,
+                                               uint64_t& blo, uint64_t& bhi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -123,40 +196,34 @@ __device__ __forceinline__ void block_minmax(uint64_t lo, uint64_t hi, SelShared
     hi = b > hi ? b : hi;
   }
   if (lane == 0) {
-    sh.red[wave] = lo;
-    sh.red[4 + wave] = hi;
+    sh.red64[wave] = lo;
+    sh.red64[kWaves + wave] = hi;
   }
   __syncthreads();
-  blo = sh.red[0];
-  bhi = sh.red[4];
-  for (int w = 1; w < kThreads / 64; ++w) {
-    blo = sh.red[w] < blo ? sh.red[w] : blo;
-    bhi = sh.red[4 + w] > bhi ? sh.red[4 + w] : bhi;
+  blo = sh.red64[0];
+  bhi = sh.red64[kWaves];
+  for (int w = 1; w < kWaves; ++w) {
+    blo = sh.red64[w] < blo ? sh.red64[w] : blo;
+    bhi = sh.red64[kWaves + w] > bhi ? sh.red64[kWaves + w] : bhi;
   }
   __syncthreads();
 }
 
-// Threshold T with exactly k of the n keys get(0..n-1) >= T (keys unique,
-// 1 <= k; returns 0 when fewer than k keys are nonzero).  Radix passes of up to 8 bits, starting
-// below the leading bits that all nonzero keys share, stopping as soon as the
-// threshold bin holds exactly the remaining need.
+// Exact k-th largest of the nonzero keys get(0..n) by 8-bit radix passes over
+// the 64-bit keys, starting below the leading bits that all of them share and
+// stopping once the threshold bin holds exactly the remaining need.  Requires
+// at least k nonzero keys.  `get(j)` may return zero for an empty slot.
 template <class Get>
-__device__ uint64_t kth_threshold(Get get, uint32_t n, uint32_t k, SelShared& sh) {
+__device__ uint64_t radix_kth(Get get, uint32_t n, uint32_t k, SelShared& sh) {
   const int tid = threadIdx.x;
   uint64_t lo = ~0ull, hi = 0ull;
-  uint32_t nz = 0;
-#pragma unroll 4
   for (uint32_t j = tid; j < n; j += kThreads) {
     const uint64_t c = get(j);
     if (c != 0ull && c < lo) lo = c;
     if (c > hi) hi = c;
-    nz += c != 0ull;
   }
-  uint32_t n_nonzero;
-  block_excl_scan(nz, sh.scratch, n_nonzero);
-  if (n_nonzero < k) return 0ull;  // caller falls back
   uint64_t blo, bhi;
-  block_minmax(lo, hi, sh, blo, bhi);
+  block_minmax64(lo, hi, sh, blo, bhi);
   if (blo >= bhi) return bhi;  // a single nonzero key
   const int top = 63 - __clzll((long long)(blo ^ bhi));  // highest differing bit
   int shift = top + 1;
@@ -166,18 +233,19 @@ __device__ uint64_t kth_threshold(Get get, uint32_t n, uint32_t k, SelShared& sh
     const int nb = shift < 8 ? shift : 8;
     const int nshift = shift - nb;
     const uint32_t mask = (1u << nb) - 1u;
-    sh.dh[tid] = 0u;
+    if (tid < 256) sh.hist[tid] = 0u;
     __syncthreads();
 #pragma unroll 4
     for (uint32_t j = tid; j < n; j += kThreads) {
       const uint64_t c = get(j);
-      if (shift >= 64 || (c >> shift) == prefix) atomicAdd(&sh.dh[(uint32_t)(c >> nshift) & mask], 1u);
+      if (c != 0ull && (shift >= 64 || (c >> shift) == prefix))
+        atomicAdd(&sh.hist[(uint32_t)(c >> nshift) & mask], 1u);
     }
     __syncthreads();
-    uint32_t cnt[1] = {sh.dh[tid]};
+    uint32_t cnt[1] = {tid < 256 ? sh.hist[tid] : 0u};
     uint32_t d, above;
     find_threshold_bin<1>(cnt, need, sh.scratch, d, above);
-    const uint32_t in_bin = sh.dh[d];
+    const uint32_t in_bin = sh.hist[d];
     need -= above;
     prefix = (shift >= 64 ? 0ull : (prefix << nb)) | d;
     shift = nshift;
@@ -187,147 +255,128 @@ __device__ uint64_t kth_threshold(Get get, uint32_t n, uint32_t k, SelShared& sh
   return prefix << shift;
 }
 
-// Write the selected blocks {s : key(s) >= thr, key != 0} in ascending order.
-template <class Get>
-__device__ uint32_t emit_sorted(Get get, uint32_t n_src, uint64_t thr, int64_t n_vis, int top_k,
-                                int32_t* out, SelShared& sh) {
+// The k-th largest of the nonzero keys in key[0..KPT) of every thread and in
+// sh.xk[0..n_x); 0 when fewer than k keys are nonzero.  1 <= k.
+__device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t n_x, uint32_t k,
+                                            SelShared& sh) {
   const int tid = threadIdx.x;
-  uint32_t emitted = 0;
-  const int64_t span = (int64_t)kBitmapWords * 32;
-  for (int64_t base = 0; base < n_vis; base += span) {
-    const int64_t len = min(span, n_vis - base);
-    const int words = (int)((len + 31) / 32);
-    for (int i = tid; i < kBitmapWords + kBitmapWords / 32; i += kThreads) sh.bitmap[i] = 0u;
-    __syncthreads();
-#pragma unroll 4
-    for (uint32_t j = tid; j < n_src; j += kThreads) {
-      const uint64_t c = get(j);
-      if (c != 0ull && c >= thr) {
-        const int64_t s = (int64_t)(~(uint32_t)c) - base;
-        if (s >= 0 && s < len) atomicOr(&sh.bitmap[(s >> 5) + (s >> 10)], 1u << (s & 31));
-      }
-    }
-    __syncthreads();
-    const int per = (words + kThreads - 1) / kThreads;
-    const int w0 = tid * per;
-    uint32_t mine = 0;
-    for (int k = 0; k < per; ++k)
-      if (w0 + k < words) mine += (uint32_t)__popc(sh.bitmap[(w0 + k) + ((w0 + k) >> 5)]);
-    uint32_t sweep_total;
-    uint32_t o = emitted + block_excl_scan(mine, sh.scratch, sweep_total);
-    for (int k = 0; k < per; ++k) {
-      if (w0 + k >= words) break;
-      uint32_t bits = sh.bitmap[(w0 + k) + ((w0 + k) >> 5)];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        if (o < (uint32_t)top_k) out[o] = (int32_t)(base + (int64_t)(w0 + k) * 32 + b);
-        ++o;
-      }
-    }
-    emitted += sweep_total;
-    __syncthreads();
-  }
-  return emitted;
-}
-
-constexpr int KPT = kPoolCap / kThreads;  // pool keys per thread
-
-__device__ __forceinline__ uint32_t bm_index(uint32_t w) { return w + (w >> 5); }
-
-// Threshold T with exactly k of the keys >= T, for keys held in registers
-// (key[i], i < KPT; zero = empty).  Returns 0 when fewer than k keys are
-// nonzero.  Digit histograms are kept per wave, so a skewed digit only
-// contends within a wave.
-__device__ __forceinline__ uint64_t kth_regs(const uint64_t (&key)[KPT], uint32_t k, SelShared& sh) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  uint64_t lo = ~0ull, hi = 0ull;
   uint32_t nz = 0;
+  float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const uint64_t c = key[i];
-    if (c != 0ull && c < lo) lo = c;
-    if (c > hi) hi = c;
-    nz += c != 0ull;
-  }
-  uint32_t n_nonzero;
-  block_excl_scan(nz, sh.scratch, n_nonzero);
-  if (n_nonzero < k) return 0ull;
-  uint64_t blo, bhi;
-  block_minmax(lo, hi, sh, blo, bhi);
-  if (blo >= bhi) return bhi;
-  const int top = 63 - __clzll((long long)(blo ^ bhi));
-  int shift = top + 1;
-  uint64_t prefix = shift >= 64 ? 0ull : (bhi >> shift);
-  uint32_t need = k;
-  for (int pass = 0; pass < 9 && shift > 0; ++pass) {
-    const int nb = shift < 8 ? shift : 8;
-    const int nshift = shift - nb;
-    const uint32_t mask = (1u << nb) - 1u;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) sh.dh4[w][tid] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint64_t c = key[i];
-      if (c != 0ull && (shift >= 64 || (c >> shift) == prefix))
-        atomicAdd(&sh.dh4[wave][(uint32_t)(c >> nshift) & mask], 1u);
+    if (key[i] != 0ull) {
+      const float v = key_value(key[i]);
+      ++nz;
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
     }
-    __syncthreads();
-    uint32_t cnt1[1] = {sh.dh4[0][tid] + sh.dh4[1][tid] + sh.dh4[2][tid] + sh.dh4[3][tid]};
-    sh.dh[tid] = cnt1[0];
-    uint32_t d, above;
-    find_threshold_bin<1>(cnt1, need, sh.scratch, d, above);
-    const uint32_t in_bin = sh.dh[d];
-    need -= above;
-    prefix = (shift >= 64 ? 0ull : (prefix << nb)) | d;
-    shift = nshift;
-    __syncthreads();
-    if (in_bin == need) break;
   }
-  return prefix << shift;
+  for (uint32_t j = tid; j < n_x; j += kThreads) {
+    const float v = key_value(sh.xk[j]);
+    ++nz;
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  uint32_t n_nz;
+  float blo, bhi;
+  block_count_range(nz, lo, hi, sh, n_nz, blo, bhi);
+  if (n_nz < k) return 0ull;
+  const float s = (float)kBins / (bhi - blo);  // +inf when all scores are equal
+  bool crowded = !(s > 0.0f && s < INFINITY);
+  if (!crowded) {
+    for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
+    if (tid == 0) sh.n_list = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (key[i] != 0ull) atomicAdd(&sh.hist[key_bin(key[i], blo, s)], 1u);
+    for (uint32_t j = tid; j < n_x; j += kThreads)
+      atomicAdd(&sh.hist[key_bin(sh.xk[j], blo, s)], 1u);
+    __syncthreads();
+    uint32_t c[2] = {sh.hist[2 * tid], sh.hist[2 * tid + 1]};
+    uint32_t b, above;
+    find_threshold_bin<2>(c, k, sh.scratch, b, above);
+    const uint32_t need = k - above;
+    const uint32_t in_bin = sh.hist[b];
+    crowded = in_bin > (uint32_t)kListCap;
+    if (!crowded) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        wave_append(key[i] != 0ull && key_bin(key[i], blo, s) == b, key[i], sh.list, &sh.n_list,
+                    kListCap);
+      for (uint32_t j0 = 0; j0 < n_x; j0 += kThreads) {
+        const uint32_t j = j0 + tid;
+        const uint64_t v = j < n_x ? sh.xk[j] : 0ull;
+        wave_append(j < n_x && key_bin(v, blo, s) == b, v, sh.list, &sh.n_list, kListCap);
+      }
+      __syncthreads();
+      if ((uint32_t)tid < in_bin) {
+        const uint64_t v = sh.list[tid];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < in_bin; ++j) r += sh.list[j] > v ? 1u : 0u;
+        if (r == need - 1u) sh.thr = v;
+      }
+      __syncthreads();
+      const uint64_t t = sh.thr;
+      __syncthreads();
+      return t;
+    }
+  }
+  // ties or tightly clustered scores: exact radix select over all the keys
+  auto get = [&](uint32_t j) -> uint64_t {
+    if (j < (uint32_t)kPoolCap) {
+      // register slot of j is (thread j % kThreads, index j / kThreads); only
+      // the calling thread's own slots are ever asked for
+      const int i = (int)(j / kThreads);
+      uint64_t v = 0ull;
+#pragma unroll
+      for (int q = 0; q < KPT; ++q)
+        if (q == i) v = key[q];
+      return v;
+    }
+    return sh.xk[j - kPoolCap];
+  };
+  return radix_kth(get, (uint32_t)kPoolCap + n_x, k, sh);
 }
 
-// Write {block of key : key >= thr, key != 0} (keys in registers) in
-// ascending block order: mark a padded LDS bitmap, then every thread scans a
-// contiguous run of words and emits its bits at its prefix-sum offset.
-__device__ __forceinline__ uint32_t emit_regs(const uint64_t (&key)[KPT], uint64_t thr, int64_t n_vis, int top_k,
-                              int32_t* out, SelShared& sh) {
+// Marks {block of key : key >= thr, key != 0} of the keys in registers, the
+// LDS extras and (if any) the row, in the bitmap, then writes them in
+// ascending block order at out[emitted..] (at most top_k in all).
+template <class Mark>
+__device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int top_k, int32_t* out,
+                                                SelShared& sh) {
   const int tid = threadIdx.x;
   uint32_t emitted = 0;
   const int64_t span = (int64_t)kBitmapWords * 32;
+  constexpr int WPT = kBitmapWords / kThreads;  // bitmap words per thread
   for (int64_t base = 0; base < n_vis; base += span) {
     const int64_t len = min(span, n_vis - base);
-    const int words = (int)((len + 31) / 32);
-    for (int i = tid; i < kBitmapWords + kBitmapWords / 32; i += kThreads) sh.bitmap[i] = 0u;
+    u32x4* bm4 = reinterpret_cast<u32x4*>(sh.bitmap);
+    for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint64_t c = key[i];
-      if (c != 0ull && c >= thr) {
-        const int64_t s = (int64_t)(~(uint32_t)c) - base;
-        if (s >= 0 && s < len) atomicOr(&sh.bitmap[bm_index((uint32_t)(s >> 5))], 1u << (s & 31));
-      }
-    }
+    mark(base, len);
     __syncthreads();
-    const int per = (words + kThreads - 1) / kThreads;
-    const int w0 = tid * per;
-    uint32_t wv[32];
+    uint32_t wv[WPT];
     uint32_t mine = 0;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      wv[q] = (q < per && w0 + q < words) ? sh.bitmap[bm_index((uint32_t)(w0 + q))] : 0u;
-      mine += (uint32_t)__popc(wv[q]);
+    for (int q = 0; q < WPT / 4; ++q) {
+      const u32x4 x = bm4[tid * (WPT / 4) + q];
+      wv[4 * q + 0] = x.x;
+      wv[4 * q + 1] = x.y;
+      wv[4 * q + 2] = x.z;
+      wv[4 * q + 3] = x.w;
     }
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) mine += (uint32_t)__popc(wv[q]);
     uint32_t sweep_total;
     uint32_t o = emitted + block_excl_scan(mine, sh.scratch, sweep_total);
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < WPT; ++q) {
       uint32_t bits = wv[q];
       while (bits) {
         const int b = __ffs(bits) - 1;
         bits &= bits - 1u;
-        if (o < (uint32_t)top_k) out[o] = (int32_t)(base + (int64_t)(w0 + q) * 32 + b);
+        if (o < (uint32_t)top_k) out[o] = (int32_t)(base + (int64_t)(tid * WPT + q) * 32 + b);
         ++o;
       }
     }
@@ -337,16 +386,19 @@ __device__ __forceinline__ uint32_t emit_regs(const uint64_t (&key)[KPT], uint64
   return emitted;
 }
 
-// Keys of the LDS pool entries tid, tid + 256, ... into registers.
-__device__ __forceinline__ void pool_to_regs(const SelShared& sh, uint32_t n, uint64_t (&key)[KPT]) {
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const uint32_t j = (uint32_t)threadIdx.x + (uint32_t)i * kThreads;
-    key[i] = j < n ? sh.pool[j] : 0ull;
-  }
+__device__ __forceinline__ void mark_block(uint64_t c, int64_t base, int64_t len, SelShared& sh) {
+  const int64_t s = (int64_t)(~(uint32_t)c) - base;
+  if (s >= 0 && s < len) atomicOr(&sh.bitmap[s >> 5], 1u << (s & 31));
 }
 
-__global__ __launch_bounds__(256) void topk_select_kernel(
+__device__ __forceinline__ int64_t token_visible(const int64_t* pos, const int32_t* n_comp, int t,
+                                                 int ratio, int64_t ld) {
+  uint32_t f = 0;
+  int64_t n_vis = visible_count(pos[t], ratio, n_comp[t], &f);
+  return n_vis > ld ? ld : n_vis;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ n_comp, int ratio, int top_k,
     const uint64_t* __restrict__ cand_all, const uint32_t* __restrict__ nvalid_all,
@@ -366,134 +418,117 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
   } else if ((int64_t)k_eff == n_vis) {
     for (uint32_t j = tid; j < k_eff; j += kThreads) out[j] = (int32_t)j;
     emitted = k_eff;
-  } else if (n_vis <= kPoolCap || cand_m == 0) {
-    // ---- direct: every visible block is a key ----
-    const uint32_t n = (uint32_t)min(n_vis, (int64_t)kPoolCap);
-    if (n_vis > kPoolCap && tid == 0) report(err, CSA_DERR_BAD_META);  // no candidates for a long row
-    uint64_t key[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-      key[i] = j < n ? block_key(srow[j], j) : 0ull;
-    }
-    const uint64_t thr = kth_regs(key, k_eff, sh);
-    emitted = emit_regs(key, thr, n_vis, top_k, out, sh);
   } else {
-    // ---- candidate lists ----
-    const int G = blocks_per_wave;
-    const int m = cand_m;
-    const uint32_t nw = (uint32_t)((n_vis + G - 1) / G);
-    const uint64_t* cand = cand_all + (int64_t)t * waves_per_token * m;
-    const uint32_t* nval = nvalid_all + (int64_t)t * waves_per_token;
-    const uint32_t C = nw * (uint32_t)m;  // <= 2/3 kPoolCap by the plan
-    // the lists go straight into registers (and the LDS pool, for the
-    // re-scan); the group sizes are loaded in the same batch
     uint64_t key[KPT];
+    uint32_t n_x = 0;
+    bool global_path = false;
+    uint64_t thr = 0ull;
+    if (n_vis <= kPoolCap || cand_m == 0) {
+      // ---- direct: every visible block is a key ----
+      const uint32_t n = (uint32_t)min(n_vis, (int64_t)kPoolCap);
+      if (n_vis > kPoolCap && tid == 0) report(err, CSA_DERR_BAD_META);  // long row, no lists
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-      key[i] = j < C ? cand[j] : 0ull;
-    }
-    constexpr int NB = 8;
-    uint32_t nv[NB];  // sizes of groups tid + 256 u
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const uint32_t w = (uint32_t)u * kThreads + tid;
-      nv[u] = w < nw ? nval[w] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-      if (j < C) sh.pool[j] = key[i];
-    }
-    if (tid == 0) {
-      sh.n_ov = 0u;
-      sh.n_pool = C;
-    }
-    __syncthreads();
-    const uint64_t t1 = C >= k_eff ? kth_regs(key, k_eff, sh) : 0ull;
-    // groups that may hold unlisted blocks at or above T1
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const uint32_t w = (uint32_t)u * kThreads + tid;
-      if (w < nw) {
-        const uint64_t cut = sh.pool[w * m + m - 1];
-        if (nv[u] > (uint32_t)m && (t1 == 0ull || cut >= t1)) {
-          const uint32_t slot = atomicAdd(&sh.n_ov, 1u);
-          if (slot < (uint32_t)kMaxOv) {
-            sh.ov_w[slot] = w;
-            sh.ov_cut[slot] = cut;
-          }
-        }
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
+        key[i] = j < n ? block_key(srow[j], j) : 0ull;
       }
-    }
-    for (uint32_t w = NB * kThreads + tid; w < nw; w += kThreads) {  // very long rows
-      const uint64_t cut = sh.pool[w * m + m - 1];
-      if (nval[w] > (uint32_t)m && (t1 == 0ull || cut >= t1)) {
-        const uint32_t slot = atomicAdd(&sh.n_ov, 1u);
-        if (slot < (uint32_t)kMaxOv) {
-          sh.ov_w[slot] = w;
-          sh.ov_cut[slot] = cut;
-        }
+      thr = kth_key(key, 0, k_eff, sh);
+    } else {
+      // ---- candidate lists ----
+      const int G = blocks_per_wave;
+      const uint32_t m = (uint32_t)cand_m;
+      const uint32_t nw = (uint32_t)((n_vis + G - 1) / G);
+      const uint64_t* cand = cand_all + (int64_t)t * waves_per_token * m;
+      const uint32_t* nval = nvalid_all + (int64_t)t * waves_per_token;
+      const uint32_t C = nw * m;  // <= kPoolCap by the plan
+      // the lists go straight into registers; the size of the group whose
+      // m-th (last) key a slot holds is loaded in the same batch
+      uint32_t nv[KPT];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
+        key[i] = j < C ? cand[j] : 0ull;
+        nv[i] = (j < C && j % m == m - 1u) ? nval[j / m] : 0u;
       }
-    }
-    __syncthreads();
-    const uint32_t n_ov = sh.n_ov;
-    bool global_path = n_ov > (uint32_t)kMaxOv || t1 == 0ull;
-    uint64_t thr = t1;
-    if (!global_path && n_ov > 0) {
-      if (tid == 0) {  // prefix of the groups' block counts (n_ov <= kMaxOv)
-        uint32_t acc = 0;
-        for (uint32_t i = 0; i < n_ov; ++i) {
-          sh.ov_off[i] = acc;
-          acc += nval[sh.ov_w[i]];
-        }
-        sh.ov_off[n_ov] = acc;
+      if (tid == 0) {
+        sh.n_ov = 0u;
+        sh.n_x = 0u;
       }
       __syncthreads();
-      const uint32_t extra = sh.ov_off[n_ov];
-      if (C + extra > (uint32_t)kPoolCap) {
-        global_path = true;
-      } else {
-        constexpr int XB = 4;
-        for (uint32_t j0 = 0; j0 < extra; j0 += XB * kThreads) {
-          uint32_t blk[XB];
-          int own[XB];
+      const uint64_t t1 = C >= k_eff ? kth_key(key, 0, k_eff, sh) : 0ull;
+      // groups that may hold unlisted blocks at or above T1
 #pragma unroll
-          for (int u = 0; u < XB; ++u) {
-            const uint32_t j = j0 + u * kThreads + tid;
-            int lo = 0, hi = (int)n_ov - 1;
-            while (lo < hi) {
-              const int mid = (lo + hi + 1) >> 1;
-              if (sh.ov_off[mid] <= j) lo = mid; else hi = mid - 1;
-            }
-            own[u] = j < extra ? lo : -1;
-            blk[u] = j < extra ? sh.ov_w[lo] * (uint32_t)G + (j - sh.ov_off[lo]) : 0u;
-          }
-          float f[XB];
-#pragma unroll
-          for (int u = 0; u < XB; ++u) f[u] = own[u] >= 0 ? srow[blk[u]] : 0.0f;
-#pragma unroll
-          for (int u = 0; u < XB; ++u) {
-            if (own[u] >= 0) {
-              const uint64_t c = block_key(f[u], blk[u]);
-              if (c < sh.ov_cut[own[u]]) sh.pool[atomicAdd(&sh.n_pool, 1u)] = c;  // not yet listed
-            }
+      for (int i = 0; i < KPT; ++i) {
+        if (nv[i] > m && (t1 == 0ull || key[i] >= t1)) {
+          const uint32_t slot = atomicAdd(&sh.n_ov, 1u);
+          if (slot < (uint32_t)kMaxOv) {
+            sh.ov_w[slot] = ((uint32_t)tid + (uint32_t)i * kThreads) / m;
+            sh.ov_nv[slot] = nv[i];
+            sh.ov_cut[slot] = key[i];
           }
         }
-        __syncthreads();
-        pool_to_regs(sh, sh.n_pool, key);
-        __syncthreads();
-        thr = kth_regs(key, k_eff, sh);
-        if (thr == 0ull) global_path = true;
+      }
+      __syncthreads();
+      const uint32_t n_ov = sh.n_ov;
+      global_path = n_ov > (uint32_t)kMaxOv || t1 == 0ull;
+      thr = t1;
+      if (!global_path && n_ov > 0) {
+        const uint32_t unlisted =
+            block_sum((uint32_t)tid < n_ov ? sh.ov_nv[tid] - m : 0u, sh.scratch);
+        if (unlisted > (uint32_t)kXCap) {
+          global_path = true;
+        } else {
+          // every block of the flagged groups that is below the group's m-th
+          // key (i.e. not listed) joins the key set
+          constexpr int XB = 4;
+          const uint32_t span = n_ov * (uint32_t)G;
+          for (uint32_t e0 = 0; e0 < span; e0 += XB * kThreads) {
+            uint32_t blk[XB];
+            bool ok[XB];
+            float f[XB];
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+              const uint32_t e = e0 + (uint32_t)u * kThreads + tid;
+              const uint32_t g = e / (uint32_t)G, off = e - g * (uint32_t)G;
+              ok[u] = e < span && off < sh.ov_nv[g < n_ov ? g : 0];
+              blk[u] = ok[u] ? sh.ov_w[g] * (uint32_t)G + off : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < XB; ++u) f[u] = ok[u] ? srow[blk[u]] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+              const uint32_t e = e0 + (uint32_t)u * kThreads + tid;
+              const uint64_t c = ok[u] ? block_key(f[u], blk[u]) : 0ull;
+              const bool add = ok[u] && c < sh.ov_cut[e / (uint32_t)G];
+              wave_append(add, c, sh.xk, &sh.n_x, kXCap);
+            }
+          }
+          __syncthreads();
+          n_x = min(sh.n_x, (uint32_t)kXCap);
+          thr = kth_key(key, n_x, k_eff, sh);
+          if (thr == 0ull) global_path = true;
+        }
       }
     }
     if (!global_path) {
-      emitted = emit_regs(key, thr, n_vis, top_k, out, sh);
+      auto mark = [&](int64_t base, int64_t len) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if (key[i] != 0ull && key[i] >= thr) mark_block(key[i], base, len, sh);
+        for (uint32_t j = tid; j < n_x; j += kThreads)
+          if (sh.xk[j] >= thr) mark_block(sh.xk[j], base, len, sh);
+      };
+      emitted = emit_bitmap(mark, n_vis, top_k, out, sh);
     } else {
       auto getg = [&](uint32_t j) { return block_key(srow[j], j); };
-      const uint64_t tg = kth_threshold(getg, (uint32_t)n_vis, k_eff, sh);
-      emitted = emit_sorted(getg, (uint32_t)n_vis, tg, n_vis, top_k, out, sh);
+      const uint64_t tg = radix_kth(getg, (uint32_t)n_vis, k_eff, sh);
+      auto mark = [&](int64_t base, int64_t len) {
+        for (int64_t j = base + tid; j < base + len; j += kThreads) {
+          const uint64_t c = getg((uint32_t)j);
+          if (c >= tg) mark_block(c, base, len, sh);
+        }
+      };
+      emitted = emit_bitmap(mark, n_vis, top_k, out, sh);
     }
   }
   if (emitted > (uint32_t)top_k) emitted = (uint32_t)top_k;
@@ -502,7 +537,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
 }
 
 // Candidate lists from caller-given scores (same layout as the indexer's).
-__global__ __launch_bounds__(256) void score_cands_kernel(
+constexpr int kCandThreads = 256;
+__global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ n_comp, int ratio, int blocks_per_wave, int cand_m,
     uint64_t* __restrict__ cand, uint32_t* __restrict__ nvalid, uint32_t* __restrict__ err) {
@@ -516,8 +552,8 @@ __global__ __launch_bounds__(256) void score_cands_kernel(
     n_vis = ld;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) report(err, flags);
-  const int64_t wg = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-  const int64_t wslot = (int64_t)t * gridDim.x * (kThreads / 64) + wg;
+  const int64_t wg = (int64_t)blockIdx.x * (kCandThreads / 64) + wave;
+  const int64_t wslot = (int64_t)t * gridDim.x * (kCandThreads / 64) + wg;
   const int64_t b0 = wg * blocks_per_wave;
   const int64_t b1 = min(b0 + (int64_t)blocks_per_wave, n_vis);
   uint64_t key[KPL];
@@ -544,8 +580,8 @@ TopkPlan plan_topk(int T, int64_t ld, int top_k) {
     p.cand_m = 0;
     return p;
   }
-  // keep a third of the pool free for groups re-scanned in full
-  int m = (2 * kPoolCap) / (3 * p.waves_per_token);
+  // the lists of one token fill at most the select workgroup's registers
+  int m = kPoolCap / p.waves_per_token;
   if (m > 32) m = 32;
   if (m < 1) m = 1;
   p.cand_m = m;
@@ -569,8 +605,8 @@ hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* po
                               const int32_t* n_comp, int T, int ratio, const TopkPlan& p,
                               const TopkWs& ws, uint32_t* err, hipStream_t s) {
   if (T == 0 || p.cand_m == 0) return hipSuccess;
-  dim3 grid((unsigned)(p.waves_per_token / (kThreads / 64)), (unsigned)T);
-  hipLaunchKernelGGL(score_cands_kernel, grid, dim3(kThreads), 0, s, scores, ld, pos, n_comp,
+  dim3 grid((unsigned)(p.waves_per_token / (kCandThreads / 64)), (unsigned)T);
+  hipLaunchKernelGGL(score_cands_kernel, grid, dim3(kCandThreads), 0, s, scores, ld, pos, n_comp,
                      ratio, p.blocks_per_wave, p.cand_m, ws.cand, ws.nvalid, err);
   return hipGetLastError();
 }
