@@ -4,19 +4,23 @@
 // followed by the SWA rows; D6: the sink is a per-head logit added to the
 // softmax denominator).
 //
-// Split-K flash decoding on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16):
-//   * a workgroup = 4 waves = up to 64 query heads (16 per wave, the MFMA M);
-//     the grid is (row splits, 64-head groups, tokens);
+// Split-K flash decoding on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16), with
+// the products transposed so that each lane owns one query head:
+//   * a workgroup = 4 waves = up to 64 query heads (16 per wave, one per lane
+//     column); the grid is (row splits, 64-head groups, tokens);
 //   * rows stream through LDS in 64-row tiles; each tile is staged twice from
-//     one set of 16-byte global loads: row-major (B operand of S = Q K^T, K = D)
-//     and 8-row interleaved (B operand of O += P V, K = rows), the latter
-//     transposed in registers with v_perm so that both products read 16 bytes
-//     per lane from LDS;
-//   * fp32 online softmax in the exp2 domain, P rounded to bf16 and passed
-//     through a per-wave LDS buffer into the A-operand layout;
-//   * each split writes unnormalised partial outputs plus (max, sum); a small
-//     combine kernel merges them (and applies the sink).  With one split the
-//     workgroup writes the final output directly.
+//     one set of 16-byte global loads: row-major (A operand of S^T = K Q^T) and
+//     8-row interleaved (A operand of O^T += V^T P^T), the latter transposed in
+//     registers with v_perm so that both products read 16 bytes per lane;
+//   * S^T leaves each lane 16 scores of its own head; the fp32 online softmax
+//     (exp2 domain) needs only two cross-lane steps, and P^T goes from those
+//     registers straight into the B operand of the second product, because the
+//     interleaved V^T groups are staged in the same row order (attention does
+//     not depend on the order of its rows);
+//   * O^T leaves each lane four consecutive d of its head, stored 16 bytes at
+//     a time: unnormalised partial outputs plus (max, sum) per split, merged by
+//     a small combine kernel (which also applies the sink).  With one split
+//     the workgroup writes the final output directly.
 // The row set of token t is segment A followed by segment B, read in place, so
 // the HCA path needs no concatenation.  In the decode step the CSA rows are
 // gathered here (selected compressed rows through their block indices, then
@@ -38,10 +42,8 @@ template <int D>
 struct Layout {
   static constexpr int RM = D + 8;                   // row-major row stride (bf16)
   static constexpr int ILG = D * 8 + (D / 8) * 8;    // interleaved 8-row group stride
-  static constexpr int PS = kRT + 8;                 // P row stride
   static constexpr int RM_ELEMS = kRT * RM;
   static constexpr int IL_ELEMS = (kRT / 8) * ILG;
-  static constexpr int P_ELEMS = 4 * 16 * PS;
 };
 
 struct SegDesc {
@@ -106,12 +108,11 @@ template <int D>
 __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int tiles_per_split,
                                                            int n_splits) {
   using L = Layout<D>;
-  constexpr int KSQ = D / 32;   // k-steps of S = Q K^T
-  constexpr int NTO = D / 16;   // 16-wide output tiles
-  constexpr int DP = D / 8;     // 16-byte pieces per row
+  constexpr int KSQ = D / 32;  // k-steps of S^T = K Q^T
+  constexpr int NTO = D / 16;  // 16-wide d tiles of O^T
+  constexpr int DP = D / 8;    // 16-byte pieces per row
   __shared__ __attribute__((aligned(16))) uint16_t rm[L::RM_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t il[L::IL_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t pb[L::P_ELEMS];
   __shared__ int64_t rsrc[kRT];  // element offset of each tile row (kSegB: segment B), -1: none
 
   const int t = blockIdx.z;
@@ -119,14 +120,25 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, quad = lane >> 4;
-  const int h0 = blockIdx.y * kHeadsPerWg + wave * 16;
+  const int h = blockIdx.y * kHeadsPerWg + wave * 16 + li;  // this lane's query head
 
-  // selected block indices of the first tile, loaded before anything they
-  // would wait on (idx rows always hold sel_stride entries)
+  // Everything the first tile waits on is loaded up front: its selected block
+  // indices (idx rows always hold sel_stride entries), Q, the row metadata.
   int32_t pidx = 0;
   const int row_begin = split * tiles_per_split * kRT;
   if (p.sel_idx != nullptr && tid < kRT)
     pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(row_begin + tid, p.sel_stride - 1)];
+  // Q as the B operand of S^T = K Q^T: lane holds Q[h][ks*32 + quad*8 .. +8].
+  bf16x8 qa[KSQ];
+  {
+    const uint16_t* qh = p.q + ((int64_t)t * p.n_heads + h) * D + quad * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (h < p.n_heads) v = *reinterpret_cast<const u32x4*>(qh + ks * 32);
+      qa[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
   uint32_t flags = 0;
   const SegDesc sd = token_rows(p, t, flags);
   if (split == 0 && blockIdx.y == 0 && tid == 0) {
@@ -136,30 +148,13 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   flags = 0;
   const int n_rows = sd.alen + sd.blen;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
-
-  // Q (A operand): lane holds head h0+li, d = ks*32 + quad*8 .. +8.
-  bf16x8 qa[KSQ];
-  {
-    const int h = h0 + li;
-    const uint16_t* qh = p.q + ((int64_t)t * p.n_heads + h) * D + quad * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (h < p.n_heads) v = *reinterpret_cast<const u32x4*>(qh + ks * 32);
-      qa[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
   const float sl2 = p.scale * kLog2e;
 
+  // o[n][r] = O^T[d = n*16 + 4*quad + r][head h] (unnormalised)
   f32x4 o[NTO];
 #pragma unroll
   for (int n = 0; n < NTO; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
+  float m_run = -INFINITY, l_run = 0.f;
 
   const uint16_t* kv_a = p.kv_a;
   const uint16_t* kv_b = p.kv_b;
@@ -169,7 +164,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     // index (gather mode) or segment B, into an LDS table ----
     if (tid < kRT) {
       const int rr = r0 + tid;
-      int64_t o = -1;
+      int64_t src = -1;
       if (rr < row_end) {
         if (rr < sd.alen) {
           int64_t ar = sd.a0 + rr;
@@ -180,20 +175,24 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
               ar = -1;
             }
           }
-          o = ar < 0 ? -1 : ar * D;
+          src = ar < 0 ? -1 : ar * D;
         } else {
-          o = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
+          src = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
         }
       }
-      rsrc[tid] = o;
+      rsrc[tid] = src;
       // prefetch the next tile's block indices
       if (p.sel_idx != nullptr && r0 + kRT < row_end)
         pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(r0 + kRT + tid, p.sel_stride - 1)];
     }
     __syncthreads();
-    // ---- stage the tile: 8x8 (rows x d) blocks; all loads issued first ----
-    constexpr int NB = (kRT / 8) * DP;             // 8x8 blocks per tile
-    constexpr int BPTH = (NB + 255) / 256;         // blocks per thread
+    // ---- stage the tile.  The P V product takes its 32 rows per k-step in
+    // the order the S^T accumulators hold them, so 8-row group g = 4*kp + qg
+    // is rows 32*kp + 16*(j/4) + 4*qg + j%4, j < 8.  Each thread loads one
+    // 8x8 (rows x d) block of a group, writes it row-major (A operand of S^T)
+    // and transposed (A operand of O^T), and copies it to all_kv. ----
+    constexpr int NB = (kRT / 8) * DP;      // 8x8 blocks per tile
+    constexpr int BPTH = (NB + 255) / 256;  // blocks per thread
     u32x4 rows[BPTH][8];
 #pragma unroll
     for (int q = 0; q < BPTH; ++q) {
@@ -201,11 +200,12 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
       const int g = b / DP, dp = b - g * DP;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int64_t o = b < NB ? rsrc[g * 8 + k] : -1;
+        const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
+        const int64_t src = b < NB ? rsrc[row] : -1;
         rows[q][k] = u32x4{0u, 0u, 0u, 0u};
-        if (o >= 0) {
-          const uint16_t* base = (o & kSegB) ? kv_b : kv_a;
-          rows[q][k] = *reinterpret_cast<const u32x4*>(base + (o & ~kSegB) + dp * 8);
+        if (src >= 0) {
+          const uint16_t* base = (src & kSegB) ? kv_b : kv_a;
+          rows[q][k] = *reinterpret_cast<const u32x4*>(base + (src & ~kSegB) + dp * 8);
         }
       }
     }
@@ -215,8 +215,13 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
       if (b >= NB) break;
       const int g = b / DP, dp = b - g * DP;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        *reinterpret_cast<u32x4*>(&rm[(g * 8 + k) * L::RM + dp * 8]) = rows[q][k];
+      for (int k = 0; k < 8; ++k) {
+        const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
+        *reinterpret_cast<u32x4*>(&rm[row * L::RM + dp * 8]) = rows[q][k];
+        if (p.copy_out != nullptr && r0 + row < row_end)
+          *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + r0 + row) * D +
+                                    dp * 8) = rows[q][k];
+      }
       uint16_t* ilg = &il[g * L::ILG + dp * 8 * 8 + dp * 8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -232,213 +237,230 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     }
     __syncthreads();
 
-    // ---- S = Q K^T for 16 heads x 64 rows ----
+    // ---- S^T = K Q^T for 64 rows x this wave's 16 heads.  The K fragments
+    // of k-step ks+1 are read from LDS while the MFMAs of ks run. ----
     f32x4 s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8 kb[2][4];
+      auto read_k = [&](int ks, bf16x8 (&dst)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
+        for (int nt = 0; nt < 4; ++nt)
+          dst[nt] = *reinterpret_cast<const bf16x8*>(&rm[(nt * 16 + li) * L::RM + ks * 32 + quad * 8]);
+      };
+      read_k(0, kb[0]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&rm[(nt * 16 + li) * L::RM + ks * 32 + quad * 8]);
-        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, s[nt], 0, 0, 0);
+      for (int ks = 0; ks < KSQ; ++ks) {
+        if (ks + 1 < KSQ) read_k(ks + 1, kb[(ks + 1) & 1]);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1][nt], qa[ks], s[nt], 0, 0, 0);
       }
     }
-    // s[nt][r] = S[head 4*quad + r][row r0 + nt*16 + li]
+    // s[nt][r] = S[head h][row r0 + nt*16 + 4*quad + r]
 
-    // ---- online softmax (exp2 domain) ----
+    // ---- online softmax (exp2 domain), one head per lane ----
     float x[4][4];
-    float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float mloc = -INFINITY;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const bool valid = r0 + nt * 16 + li < row_end;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        const bool valid = r0 + nt * 16 + 4 * quad + r < row_end;
         x[nt][r] = valid ? s[nt][r] * sl2 : -INFINITY;
-        mloc[r] = fmaxf(mloc[r], x[nt][r]);
+        mloc = fmaxf(mloc, x[nt][r]);
       }
     }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float mnew = fmaxf(m_run, mloc);
+    const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run - mnew);
+    float lsum = 0.f;
+    // P^T (B operand of O^T): k-step kp takes tiles 2kp, 2kp+1 of this lane
+    bf16x8 pb[2];
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
+    for (int kp = 0; kp < 2; ++kp) {
+      uint32_t w[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mloc[r] = fmaxf(mloc[r], __shfl_xor(mloc[r], off));
-    }
-    float alpha[4], mnew[4], lsum[4];
+      for (int hh = 0; hh < 2; ++hh) {
+        float pv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mnew[r] = fmaxf(m_run[r], mloc[r]);
-      alpha[r] = (mnew[r] == -INFINITY) ? 1.f : exp2f(m_run[r] - mnew[r]);
-      lsum[r] = 0.f;
-    }
-    uint16_t* pw = &pb[wave * 16 * L::PS];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = (x[nt][r] == -INFINITY) ? 0.f : exp2f(x[nt][r] - mnew[r]);
-        lsum[r] += pv;
-        pw[(4 * quad + r) * L::PS + nt * 16 + li] = f32_to_bf16(pv);
+        for (int r = 0; r < 4; ++r) {
+          const float xv = x[2 * kp + hh][r];
+          pv[r] = (xv == -INFINITY) ? 0.f : exp2f(xv - mnew);
+          lsum += pv[r];
+        }
+        w[2 * hh + 0] = (uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16);
+        w[2 * hh + 1] = (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16);
       }
+      pb[kp] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
     }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    m_run = mnew;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lsum[r] += __shfl_xor(lsum[r], off);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      l_run[r] = l_run[r] * alpha[r] + lsum[r];
-      m_run[r] = mnew[r];
-    }
-#pragma unroll
-    for (int n = 0; n < NTO; ++n) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[n][r] *= alpha[r];
-    }
-    __syncthreads();  // P visible in the A-operand layout
+    for (int n = 0; n < NTO; ++n) o[n] *= alpha;
 
-    // ---- O += P V ----
+    // ---- O^T += V^T P^T; V^T fragments are read four d-tiles ahead ----
+    {
+      constexpr int NS = 2 * NTO;  // (kp, n) steps
+      constexpr int GB = 4;        // fragments per batch
+      bf16x8 vb[2][GB];
+      auto read_v = [&](int b, bf16x8 (&dst)[GB]) {
 #pragma unroll
-    for (int kp = 0; kp < kRT / 32; ++kp) {
-      const bf16x8 pa = *reinterpret_cast<const bf16x8*>(&pw[li * L::PS + kp * 32 + quad * 8]);
-      const uint16_t* ilg = &il[(kp * 4 + quad) * L::ILG];
+        for (int u = 0; u < GB; ++u) {
+          const int st = b * GB + u, kp = st / NTO, n = st - kp * NTO;
+          const int d = n * 16 + li;
+          dst[u] = *reinterpret_cast<const bf16x8*>(&il[(kp * 4 + quad) * L::ILG + d * 8 + (d >> 3) * 8]);
+        }
+      };
+      read_v(0, vb[0]);
 #pragma unroll
-      for (int n = 0; n < NTO; ++n) {
-        const int d = n * 16 + li;
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(ilg + d * 8 + (d >> 3) * 8);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[n], 0, 0, 0);
-      }
-    }
-    // gather mode: copy the staged rows to all_kv (off the staging critical path)
-    if (p.copy_out != nullptr) {
-      for (int c = tid; c < kRT * DP; c += 256) {
-        const int r = c / DP, dp = c - r * DP;
-        const int rr = r0 + r;
-        if (rr < row_end)
-          *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + rr) * D + dp * 8) =
-              *reinterpret_cast<const u32x4*>(&rm[r * L::RM + dp * 8]);
+      for (int b = 0; b < NS / GB; ++b) {
+        if (b + 1 < NS / GB) read_v(b + 1, vb[(b + 1) & 1]);
+#pragma unroll
+        for (int u = 0; u < GB; ++u) {
+          const int st = b * GB + u, kp = st / NTO, n = st - kp * NTO;
+          o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[b & 1][u], pb[kp], o[n], 0, 0, 0);
+        }
       }
     }
   }
 
   report(p.err, flags);
-  // ---- epilogue: o[n][r] = O[head 4*quad + r][d = n*16 + li] ----
+  // ---- epilogue: lane (li, quad) holds d = n*16 + 4*quad + r of head h ----
+  if (h >= p.n_heads) return;
   if (n_splits == 1) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = h0 + 4 * quad + r;
-      if (h >= p.n_heads) continue;
-      float M = m_run[r];
-      float Lsum = l_run[r];
-      float f = 1.f;
-      if (p.sink != nullptr) {
-        const float s2 = p.sink[h] * kLog2e;
-        const float Mn = fmaxf(M, s2);
-        f = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
-        Lsum = Lsum * f + exp2f(s2 - Mn);
-        M = Mn;
-      }
-      const float inv = Lsum > 0.f ? f / Lsum : 0.f;
-      uint16_t* oh = p.out + ((int64_t)t * p.n_heads + h) * D;
-#pragma unroll
-      for (int n = 0; n < NTO; ++n) oh[n * 16 + li] = f32_to_bf16(o[n][r] * inv);
-      if (p.lse != nullptr && li == 0)
-        p.lse[(int64_t)t * p.n_heads + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
+    float M = m_run;
+    float Lsum = l_run;
+    float f = 1.f;
+    if (p.sink != nullptr) {
+      const float s2 = p.sink[h] * kLog2e;
+      const float Mn = fmaxf(M, s2);
+      f = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+      Lsum = Lsum * f + exp2f(s2 - Mn);
+      M = Mn;
     }
+    const float inv = Lsum > 0.f ? f / Lsum : 0.f;
+    uint16_t* oh = p.out + ((int64_t)t * p.n_heads + h) * D + 4 * quad;
+#pragma unroll
+    for (int n = 0; n < NTO; ++n) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(o[n][0] * inv) | ((uint32_t)f32_to_bf16(o[n][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(o[n][2] * inv) | ((uint32_t)f32_to_bf16(o[n][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(oh + n * 16) = make_uint2(lo, hi);
+    }
+    if (p.lse != nullptr && quad == 0)
+      p.lse[(int64_t)t * p.n_heads + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
   } else {
     float* part_o = static_cast<float*>(p.ws);
     float* part_ml = part_o + (size_t)p.T * n_splits * p.n_heads * D;
+    const size_t slot = ((size_t)t * n_splits + split) * p.n_heads + h;
+    float* po = part_o + slot * D + 4 * quad;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = h0 + 4 * quad + r;
-      if (h >= p.n_heads) continue;
-      const size_t slot = ((size_t)t * n_splits + split) * p.n_heads + h;
-      float* po = part_o + slot * D;
-#pragma unroll
-      for (int n = 0; n < NTO; ++n) po[n * 16 + li] = o[n][r];
-      if (li == 0) {
-        part_ml[slot * 2 + 0] = m_run[r];
-        part_ml[slot * 2 + 1] = l_run[r];
-      }
+    for (int n = 0; n < NTO; ++n) *reinterpret_cast<f32x4*>(po + n * 16) = o[n];
+    if (quad == 0) {
+      part_ml[slot * 2 + 0] = m_run;
+      part_ml[slot * 2 + 1] = l_run;
     }
   }
 }
 
-// Merge of the split partials of one (token, head): all split weights are
-// formed at once (one split per lane), then the partial rows are accumulated
-// with their loads batched four splits at a time.
+// Merge of the split partials of one (token, head).  Wave w takes splits
+// w, w+4, ...; the first eight of each wave are loaded together with every
+// split's (max, sum), so two splits rounds cost one memory round trip.
 template <int D>
-__global__ __launch_bounds__(64) void attend_combine_kernel(AttendLaunch p, int n_splits) {
-  constexpr int EPL = D / 64;
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int n_splits) {
+  constexpr int EPL = D / 64;  // output elements per lane
+  constexpr int SG = 4;        // split groups = waves
+  constexpr int CH = 8;        // splits per group per round
   __shared__ float fw[kMaxSplits];
-  const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  __shared__ float wred[2][SG];
+  __shared__ __attribute__((aligned(16))) float red[SG][D];
+  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const float* part_o = static_cast<const float*>(p.ws);
   const float* part_ml = part_o + (size_t)p.T * n_splits * p.n_heads * D;
   const size_t slot0 = (size_t)t * n_splits * p.n_heads + h;
-  constexpr int SPL = kMaxSplits / 64;
-  float m[SPL], l[SPL];
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < SPL; ++i) {
-    const int s = lane + 64 * i;
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-    if (s < n_splits) {
-      const size_t slot = slot0 + (size_t)s * p.n_heads;
-      m[i] = part_ml[slot * 2];
-      l[i] = part_ml[slot * 2 + 1];
-      if (l[i] > 0.f) M = fmaxf(M, m[i]);
-    }
+  const size_t sstride = (size_t)p.n_heads * D;
+  const float* pbase = part_o + slot0 * D + lane * EPL;
+
+  float m_s = -INFINITY, l_s = 0.f;
+  if (tid < n_splits) {
+    const size_t slot = slot0 + (size_t)tid * p.n_heads;
+    m_s = part_ml[slot * 2];
+    l_s = part_ml[slot * 2 + 1];
   }
+  float v[CH][EPL];
+  auto load_round = [&](int c0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int s = wave + SG * (c0 + c);
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[c][j] = 0.f;
+      if (s < n_splits) {
+        const float* src = pbase + (size_t)s * sstride;
+        if constexpr (EPL % 4 == 0) {
+#pragma unroll
+          for (int j = 0; j < EPL; j += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(src + j);
+            v[c][j] = x[0];
+            v[c][j + 1] = x[1];
+            v[c][j + 2] = x[2];
+            v[c][j + 3] = x[3];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < EPL; ++j) v[c][j] = src[j];
+        }
+      }
+    }
+  };
+  load_round(0);
+
+  float M = l_s > 0.f ? m_s : -INFINITY;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) wred[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
   float s2 = -INFINITY;
   if (p.sink != nullptr) {
     s2 = p.sink[h] * kLog2e;
     M = fmaxf(M, s2);
   }
-  float Lsum = 0.f;
+  const float f = (l_s > 0.f) ? exp2f(m_s - M) : 0.f;
+  fw[tid] = f;
+  float Lp = l_s * f;
 #pragma unroll
-  for (int i = 0; i < SPL; ++i) {
-    const int s = lane + 64 * i;
-    const float f = (l[i] > 0.f) ? exp2f(m[i] - M) : 0.f;
-    Lsum += l[i] * f;
-    if (s < n_splits) fw[s] = f;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) Lsum += __shfl_xor(Lsum, off);
-  if (p.sink != nullptr) Lsum += exp2f(s2 - M);
+  for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
+  if (lane == 0) wred[1][wave] = Lp;
   __syncthreads();
+  float Lsum = wred[1][0] + wred[1][1] + wred[1][2] + wred[1][3];
+  if (p.sink != nullptr) Lsum += exp2f(s2 - M);
+
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  const float* pb = part_o + slot0 * D + lane * EPL;
-  const size_t sstride = (size_t)p.n_heads * D;
-  for (int s0 = 0; s0 < n_splits; s0 += 4) {
-    float v[4][EPL];
+  for (int c0 = 0; wave + SG * c0 < n_splits; c0 += CH) {
+    if (c0 > 0) load_round(c0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u;
+    for (int c = 0; c < CH; ++c) {
+      const int s = wave + SG * (c0 + c);
+      const float wgt = s < n_splits ? fw[s] : 0.f;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) v[u][j] = 0.f;
-      if (s < n_splits && fw[s] != 0.f) {
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) v[u][j] = pb[(size_t)s * sstride + j];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int s = s0 + u;
-      const float f = s < n_splits ? fw[s] : 0.f;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[j] += f * v[u][j];
+      for (int j = 0; j < EPL; ++j) acc[j] += wgt * v[c][j];
     }
   }
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  uint16_t* oh = p.out + ((size_t)t * p.n_heads + h) * D + lane * EPL;
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) oh[j] = f32_to_bf16(acc[j] * inv);
-  if (p.lse != nullptr && lane == 0)
+  for (int j = 0; j < EPL; ++j) red[wave][lane * EPL + j] = acc[j];
+  __syncthreads();
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  uint16_t* oh = p.out + ((size_t)t * p.n_heads + h) * D;
+  for (int e = tid; e < D; e += 256)
+    oh[e] = f32_to_bf16((red[0][e] + red[1][e] + red[2][e] + red[3][e]) * inv);
+  if (p.lse != nullptr && tid == 0)
     p.lse[(size_t)t * p.n_heads + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
@@ -469,7 +491,7 @@ hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.n_splits == 1) return e;
   hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),
-                     dim3(64), 0, s, a, sp.n_splits);
+                     dim3(256), 0, s, a, sp.n_splits);
   return hipGetLastError();
 }
 

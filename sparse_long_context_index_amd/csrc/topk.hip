@@ -46,6 +46,7 @@ constexpr int kXCap = 4096;               // keys of re-scanned groups (LDS)
 constexpr int kListCap = 1024;            // threshold-bin keys ranked exactly
 constexpr int kMaxOv = 512;               // groups re-scanned before falling back
 constexpr int kBitmapWords = 8192;        // 262,144 blocks per emission sweep
+constexpr int kMaxTopK = 2048;
 static_assert(KPT * kThreads == kPoolCap, "pool must split evenly");
 static_assert(kBitmapWords % (8 * kThreads) == 0, "8 bitmap words per thread");
 
@@ -57,9 +58,13 @@ struct SelShared {
   uint32_t ov_w[kMaxOv];
   uint32_t ov_nv[kMaxOv];
   uint64_t ov_cut[kMaxOv];
+  int32_t outl[kMaxTopK];                 // the selection, ascending, before the output copy
   uint32_t scratch[2 * kWaves + 8];
+  uint32_t rc[kWaves];                    // per-wave count / range of kth_key
+  float rlo[kWaves], rhi[kWaves];
+  uint32_t fb_w[kWaves];                  // per-wave bin totals of kth_key
+  uint32_t fb_bin, fb_above;
   uint64_t red64[2 * kWaves];
-  float redf[2 * kWaves];
   uint64_t thr;
   uint32_t n_x, n_ov, n_list;
 };
@@ -157,33 +162,6 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
   return total;
 }
 
-// Block-wide count, min and max (of the scores) of the nonzero keys.
-__device__ __forceinline__ void block_count_range(uint32_t n, float lo, float hi, SelShared& sh,
-                                                  uint32_t& bn, float& blo, float& bhi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    n += __shfl_xor(n, off);
-    lo = fminf(lo, __shfl_xor(lo, off));
-    hi = fmaxf(hi, __shfl_xor(hi, off));
-  }
-  if (lane == 0) {
-    sh.scratch[wave] = n;
-    sh.redf[wave] = lo;
-    sh.redf[kWaves + wave] = hi;
-  }
-  __syncthreads();
-  bn = 0;
-  blo = INFINITY;
-  bhi = -INFINITY;
-  for (int w = 0; w < kWaves; ++w) {
-    bn += sh.scratch[w];
-    blo = fminf(blo, sh.redf[w]);
-    bhi = fmaxf(bhi, sh.redf[kWaves + w]);
-  }
-  __syncthreads();
-}
-
 // Block-wide min over nonzero keys and max of 64-bit keys.
 __device__ __forceinline__ void block_minmax64(uint64_t lo, uint64_t hi, SelShared& sh,
                                                uint64_t& blo, uint64_t& bhi) {
@@ -256,10 +234,13 @@ __device__ uint64_t radix_kth(Get get, uint32_t n, uint32_t k, SelShared& sh) {
 }
 
 // The k-th largest of the nonzero keys in key[0..KPT) of every thread and in
-// sh.xk[0..n_x); 0 when fewer than k keys are nonzero.  1 <= k.
+// sh.xk[0..n_x); 0 when fewer than k keys are nonzero.  1 <= k.  Each phase
+// writes its own LDS slots, so six barriers separate the phases (a barrier
+// between a phase's reads and the next call's writes always intervenes).
 __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t n_x, uint32_t k,
                                             SelShared& sh) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- count and score range of the nonzero keys; clear the histogram ----
   uint32_t nz = 0;
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
@@ -277,29 +258,67 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
     lo = fminf(lo, v);
     hi = fmaxf(hi, v);
   }
-  uint32_t n_nz;
-  float blo, bhi;
-  block_count_range(nz, lo, hi, sh, n_nz, blo, bhi);
+  for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
+  if (tid == 0) sh.n_list = 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    nz += __shfl_xor(nz, off);
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  if (lane == 0) {
+    sh.rc[wave] = nz;
+    sh.rlo[wave] = lo;
+    sh.rhi[wave] = hi;
+  }
+  __syncthreads();
+  uint32_t n_nz = 0;
+  float blo = INFINITY, bhi = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    n_nz += sh.rc[w];
+    blo = fminf(blo, sh.rlo[w]);
+    bhi = fmaxf(bhi, sh.rhi[w]);
+  }
   if (n_nz < k) return 0ull;
   const float s = (float)kBins / (bhi - blo);  // +inf when all scores are equal
   bool crowded = !(s > 0.0f && s < INFINITY);
   if (!crowded) {
-    for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
-    if (tid == 0) sh.n_list = 0u;
-    __syncthreads();
+    // ---- histogram of the linear bins ----
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
       if (key[i] != 0ull) atomicAdd(&sh.hist[key_bin(key[i], blo, s)], 1u);
     for (uint32_t j = tid; j < n_x; j += kThreads)
       atomicAdd(&sh.hist[key_bin(sh.xk[j], blo, s)], 1u);
     __syncthreads();
-    uint32_t c[2] = {sh.hist[2 * tid], sh.hist[2 * tid + 1]};
-    uint32_t b, above;
-    find_threshold_bin<2>(c, k, sh.scratch, b, above);
-    const uint32_t need = k - above;
+    // ---- the bin b with (keys in bins > b) < k <= (keys in bins >= b);
+    // thread i owns bins 2i, 2i+1 ----
+    const uint32_t c0 = sh.hist[2 * tid], c1 = sh.hist[2 * tid + 1];
+    const uint32_t tot = c0 + c1;
+    uint32_t x = tot;  // inclusive suffix sum within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_down(x, d);
+      if (lane + d < 64) x += y;
+    }
+    if (lane == 0) sh.fb_w[wave] = x;
+    __syncthreads();
+    uint32_t acc = x - tot;
+    for (int wv = wave + 1; wv < kWaves; ++wv) acc += sh.fb_w[wv];
+    if (acc < k && acc + c1 >= k) {
+      sh.fb_bin = 2u * tid + 1u;
+      sh.fb_above = acc;
+    } else if (acc + c1 < k && acc + c1 + c0 >= k) {
+      sh.fb_bin = 2u * tid;
+      sh.fb_above = acc + c1;
+    }
+    __syncthreads();
+    const uint32_t b = sh.fb_bin;
+    const uint32_t need = k - sh.fb_above;
     const uint32_t in_bin = sh.hist[b];
     crowded = in_bin > (uint32_t)kListCap;
     if (!crowded) {
+      // ---- exact rank among the keys of bin b ----
 #pragma unroll
       for (int i = 0; i < KPT; ++i)
         wave_append(key[i] != 0ull && key_bin(key[i], blo, s) == b, key[i], sh.list, &sh.n_list,
@@ -317,9 +336,7 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
         if (r == need - 1u) sh.thr = v;
       }
       __syncthreads();
-      const uint64_t t = sh.thr;
-      __syncthreads();
-      return t;
+      return sh.thr;
     }
   }
   // ties or tightly clustered scores: exact radix select over all the keys
@@ -340,20 +357,23 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
 }
 
 // Marks {block of key : key >= thr, key != 0} of the keys in registers, the
-// LDS extras and (if any) the row, in the bitmap, then writes them in
-// ascending block order at out[emitted..] (at most top_k in all).
+// LDS extras and (if any) the row, in the bitmap (already clear on entry),
+// then lists them in ascending block order at sh.outl[0..top_k); returns how
+// many were marked.
 template <class Mark>
-__device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int top_k, int32_t* out,
+__device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int top_k,
                                                 SelShared& sh) {
   const int tid = threadIdx.x;
   uint32_t emitted = 0;
   const int64_t span = (int64_t)kBitmapWords * 32;
   constexpr int WPT = kBitmapWords / kThreads;  // bitmap words per thread
+  u32x4* bm4 = reinterpret_cast<u32x4*>(sh.bitmap);
   for (int64_t base = 0; base < n_vis; base += span) {
     const int64_t len = min(span, n_vis - base);
-    u32x4* bm4 = reinterpret_cast<u32x4*>(sh.bitmap);
-    for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    if (base > 0) {
+      for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+    }
     mark(base, len);
     __syncthreads();
     uint32_t wv[WPT];
@@ -374,9 +394,9 @@ __device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int to
     for (int q = 0; q < WPT; ++q) {
       uint32_t bits = wv[q];
       while (bits) {
-        const int b = __ffs(bits) - 1;
+        const int bb = __ffs(bits) - 1;
         bits &= bits - 1u;
-        if (o < (uint32_t)top_k) out[o] = (int32_t)(base + (int64_t)(tid * WPT + q) * 32 + b);
+        if (o < (uint32_t)top_k) sh.outl[o] = (int32_t)(base + (int64_t)(tid * WPT + q) * 32 + bb);
         ++o;
       }
     }
@@ -391,13 +411,6 @@ __device__ __forceinline__ void mark_block(uint64_t c, int64_t base, int64_t len
   if (s >= 0 && s < len) atomicOr(&sh.bitmap[s >> 5], 1u << (s & 31));
 }
 
-__device__ __forceinline__ int64_t token_visible(const int64_t* pos, const int32_t* n_comp, int t,
-                                                 int ratio, int64_t ld) {
-  uint32_t f = 0;
-  int64_t n_vis = visible_count(pos[t], ratio, n_comp[t], &f);
-  return n_vis > ld ? ld : n_vis;
-}
-
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ n_comp, int ratio, int top_k,
@@ -407,19 +420,50 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  const int64_t n_vis = token_visible(pos, n_comp, t, ratio, ld);
-  const uint32_t k_eff = (uint32_t)(n_vis < (int64_t)top_k ? n_vis : (int64_t)top_k);
   int32_t* out = idx + (int64_t)t * top_k;
   const float* srow = scores + (int64_t)t * ld;
-  uint32_t emitted = 0;
 
+  // Loads that do not depend on the row length go out together: the token's
+  // metadata and, when there are candidate lists, every list of the token
+  // (the indexer writes all of them, zero keys for waves without blocks) with
+  // the size of the group whose m-th key each slot holds.
+  const int64_t pos_t = pos[t];
+  const int32_t ncomp_t = n_comp[t];
+  const uint32_t m = cand_m > 0 ? (uint32_t)cand_m : 1u;
+  const uint32_t CT = cand_m > 0 ? min((uint32_t)waves_per_token * m, (uint32_t)kPoolCap) : 0u;
+  const uint64_t* cand = cand_all + (int64_t)t * waves_per_token * cand_m;
+  const uint32_t* nval = nvalid_all + (int64_t)t * waves_per_token;
+  uint64_t key[KPT];
+  uint32_t nv[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
+    key[i] = j < CT ? cand[j] : 0ull;
+    nv[i] = (j < CT && j % m == m - 1u) ? nval[j / m] : 0u;
+  }
+  // the emission bitmap is cleared while those loads are in flight
+  {
+    u32x4* bm4 = reinterpret_cast<u32x4*>(sh.bitmap);
+    for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid == 0) {
+    sh.n_ov = 0u;
+    sh.n_x = 0u;
+  }
+  uint32_t f = 0;
+  int64_t n_vis = visible_count(pos_t, ratio, ncomp_t, &f);
+  if (n_vis > ld) n_vis = ld;
+  const uint32_t k_eff = (uint32_t)(n_vis < (int64_t)top_k ? n_vis : (int64_t)top_k);
+  __syncthreads();
+
+  uint32_t emitted = 0;
+  bool listed = false;  // the selection is in sh.outl
   if (k_eff == 0) {
     emitted = 0;
   } else if ((int64_t)k_eff == n_vis) {
-    for (uint32_t j = tid; j < k_eff; j += kThreads) out[j] = (int32_t)j;
-    emitted = k_eff;
+    emitted = k_eff;  // every visible block
   } else {
-    uint64_t key[KPT];
+    listed = true;
     uint32_t n_x = 0;
     bool global_path = false;
     uint64_t thr = 0ull;
@@ -431,30 +475,22 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
       for (int i = 0; i < KPT; ++i) {
         const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
         key[i] = j < n ? block_key(srow[j], j) : 0ull;
+        nv[i] = 0u;
       }
       thr = kth_key(key, 0, k_eff, sh);
     } else {
-      // ---- candidate lists ----
+      // ---- candidate lists of the nw groups that cover the row ----
       const int G = blocks_per_wave;
-      const uint32_t m = (uint32_t)cand_m;
       const uint32_t nw = (uint32_t)((n_vis + G - 1) / G);
-      const uint64_t* cand = cand_all + (int64_t)t * waves_per_token * m;
-      const uint32_t* nval = nvalid_all + (int64_t)t * waves_per_token;
-      const uint32_t C = nw * m;  // <= kPoolCap by the plan
-      // the lists go straight into registers; the size of the group whose
-      // m-th (last) key a slot holds is loaded in the same batch
-      uint32_t nv[KPT];
+      const uint32_t C = min(nw * m, CT);
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-        key[i] = j < C ? cand[j] : 0ull;
-        nv[i] = (j < C && j % m == m - 1u) ? nval[j / m] : 0u;
+        if (j >= C) {
+          key[i] = 0ull;
+          nv[i] = 0u;
+        }
       }
-      if (tid == 0) {
-        sh.n_ov = 0u;
-        sh.n_x = 0u;
-      }
-      __syncthreads();
       const uint64_t t1 = C >= k_eff ? kth_key(key, 0, k_eff, sh) : 0ull;
       // groups that may hold unlisted blocks at or above T1
 #pragma unroll
@@ -485,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
           for (uint32_t e0 = 0; e0 < span; e0 += XB * kThreads) {
             uint32_t blk[XB];
             bool ok[XB];
-            float f[XB];
+            float fv[XB];
 #pragma unroll
             for (int u = 0; u < XB; ++u) {
               const uint32_t e = e0 + (uint32_t)u * kThreads + tid;
@@ -494,11 +530,11 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
               blk[u] = ok[u] ? sh.ov_w[g] * (uint32_t)G + off : 0u;
             }
 #pragma unroll
-            for (int u = 0; u < XB; ++u) f[u] = ok[u] ? srow[blk[u]] : 0.0f;
+            for (int u = 0; u < XB; ++u) fv[u] = ok[u] ? srow[blk[u]] : 0.0f;
 #pragma unroll
             for (int u = 0; u < XB; ++u) {
               const uint32_t e = e0 + (uint32_t)u * kThreads + tid;
-              const uint64_t c = ok[u] ? block_key(f[u], blk[u]) : 0ull;
+              const uint64_t c = ok[u] ? block_key(fv[u], blk[u]) : 0ull;
               const bool add = ok[u] && c < sh.ov_cut[e / (uint32_t)G];
               wave_append(add, c, sh.xk, &sh.n_x, kXCap);
             }
@@ -518,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
         for (uint32_t j = tid; j < n_x; j += kThreads)
           if (sh.xk[j] >= thr) mark_block(sh.xk[j], base, len, sh);
       };
-      emitted = emit_bitmap(mark, n_vis, top_k, out, sh);
+      emitted = emit_bitmap(mark, n_vis, top_k, sh);
     } else {
       auto getg = [&](uint32_t j) { return block_key(srow[j], j); };
       const uint64_t tg = radix_kth(getg, (uint32_t)n_vis, k_eff, sh);
@@ -528,11 +564,13 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
           if (c >= tg) mark_block(c, base, len, sh);
         }
       };
-      emitted = emit_bitmap(mark, n_vis, top_k, out, sh);
+      emitted = emit_bitmap(mark, n_vis, top_k, sh);
     }
   }
   if (emitted > (uint32_t)top_k) emitted = (uint32_t)top_k;
-  for (uint32_t i = emitted + tid; i < (uint32_t)top_k; i += kThreads) out[i] = -1;
+  // one coalesced pass writes the selection and the -1 padding
+  for (uint32_t i = tid; i < (uint32_t)top_k; i += kThreads)
+    out[i] = i < emitted ? (listed ? sh.outl[i] : (int32_t)i) : -1;
   if (tid == 0) count[t] = (int32_t)emitted;
 }
 
