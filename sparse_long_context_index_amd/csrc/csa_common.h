@@ -33,32 +33,69 @@ __device__ __forceinline__ uint64_t block_key(float f, uint32_t s) {
   return ((uint64_t)score_key(f) << 32) | (uint32_t)(~s);
 }
 
-// Wave-level top-m of composite keys held by the lanes (KPL per lane, zero =
-// empty): the m largest keys, descending, zero-padded, are written by lane 0
-// to out[0..m).  The keys are consumed.
+// Largest value over the wave: DPP max steps within each row of 16 lanes
+// (quad swaps, half-row and row mirrors), then row broadcasts carry the row
+// maxima up to lane 63, which holds the total.  Register-to-register only.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half-row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Wave-level top-m of the blocks whose scores the lanes hold: for q < KPL,
+// lane L holds score sc[q] of block blk[q] where ok[q].  Block indices must
+// ascend in (q, lane) order.  Writes the m largest composite keys (larger
+// score, then lower index) to out[0..m) in descending order, so out[m-1] is
+// the smallest key of the list; with fewer than m valid blocks the list is
+// zero-padded.  Returns the number of valid blocks.  One key per round: the
+// wave maximum of the 32-bit score keys, then the lowest (q, lane) holding it.
 template <int KPL>
-__device__ __forceinline__ void wave_top_m(uint64_t (&key)[KPL], int m, uint64_t* out) {
+__device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const bool (&ok)[KPL],
+                                               const uint32_t (&blk)[KPL], uint32_t m,
+                                               uint64_t* out) {
   const int lane = threadIdx.x & 63;
-  for (int i = 0; i < m; ++i) {
-    uint64_t lm = 0;
+  uint32_t sk[KPL];  // 0 = empty (score keys of non-NaN scores are nonzero)
+  uint32_t n_ok = 0;
 #pragma unroll
-    for (int q = 0; q < KPL; ++q) lm = key[q] > lm ? key[q] : lm;
-    uint64_t wm = lm;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint64_t o = __shfl_xor((unsigned long long)wm, off);
-      wm = o > wm ? o : wm;
-    }
-    if (lane == 0) out[i] = wm;
-    if (wm == 0) {  // wave-uniform
-      if (lane == 0)
-        for (int r = i + 1; r < m; ++r) out[r] = 0;
-      break;
-    }
-#pragma unroll
-    for (int q = 0; q < KPL; ++q)
-      if (key[q] == wm) key[q] = 0;
+  for (int q = 0; q < KPL; ++q) {
+    sk[q] = ok[q] ? score_key(sc[q]) : 0u;
+    n_ok += (uint32_t)__popcll(__ballot(ok[q]));
   }
+  const uint32_t take = n_ok < m ? n_ok : m;
+  for (uint32_t r = 0; r < take; ++r) {
+    uint32_t lm = 0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) lm = max(lm, sk[q]);
+    const uint32_t M = wave_max_u32(lm);
+    int oq = -1;
+    uint64_t mask = 0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) {
+      if (oq < 0) {  // wave-uniform
+        const uint64_t b = __ballot(sk[q] == M);
+        if (b != 0ull) {
+          oq = q;
+          mask = b;
+        }
+      }
+    }
+    if (lane == __ffsll((unsigned long long)mask) - 1) {
+      uint32_t ob = 0;
+#pragma unroll
+      for (int q = 0; q < KPL; ++q)
+        if (q == oq) {
+          ob = blk[q];
+          sk[q] = 0u;
+        }
+      out[r] = ((uint64_t)M << 32) | (uint32_t)~ob;
+    }
+  }
+  for (uint32_t i = take + (uint32_t)lane; i < m; i += 64) out[i] = 0ull;
+  return n_ok;
 }
 
 // Visible-block count of a token; flags inconsistent metadata.  Mirrors the
@@ -107,7 +144,7 @@ struct IndexScoreLaunch {
   int cand_m;
   uint32_t* err;
 };
-constexpr int kIndexWaves = 4;  // waves per indexer workgroup
+constexpr int kIndexWaves = 8;  // waves per indexer workgroup
 struct IndexPlan {
   int tiles_per_wave, wgs_per_token;
   int waves_per_token() const { return wgs_per_token * kIndexWaves; }

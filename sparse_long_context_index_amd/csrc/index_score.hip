@@ -14,17 +14,23 @@
 //
 // Decode is HBM-bound (64 flop per key byte at n_ih = 64, far below the MFMA
 // ridge), so the kernel is built around streaming the keys:
-//   * every wave walks a contiguous run of 32-block tiles; each tile is
+//   * a workgroup is eight waves, one workgroup per CU on a 1M-block row;
+//     every wave walks a contiguous run of 32-block tiles; each tile is
 //     fetched with global_load_lds_dwordx4, 1 KiB (whole key rows) per
 //     instruction, straight into a per-wave LDS buffer -- no VGPRs, fully
 //     coalesced, two tiles in flight (double buffer);
 //   * the 16-byte chunk slots of each row are XOR-swizzled by the row index,
-//     chosen through the per-lane global address, so that the MFMA B-operand
-//     reads (lane = block column, 16 bytes of that row) are bank-conflict free;
-//   * the token's queries and head weights are loaded into VGPRs and settled
-//     before the loop, so the only memory operations in flight inside it are
-//     the tile DMAs, waited for with explicit vmcnt counts; scores stay in
-//     VGPRs until the wave's tiles are done.
+//     chosen through the per-lane global address, so that the MFMA operand
+//     reads (lane = block column or head, 16 bytes of that row) are
+//     bank-conflict free;
+//   * the token's query block (the same for every wave) is brought into LDS
+//     once per workgroup by the same DMA, together with the token metadata
+//     and head weights (one round trip), instead of every wave reading it
+//     from L2; the first key tiles are issued before the one workgroup
+//     barrier, after which each wave copies its query operands to VGPRs.
+//     The only memory operations pending in the loop are then tile DMAs,
+//     waited for with explicit vmcnt counts; the tile loop is unrolled so the
+//     per-tile scores stay in VGPRs until the wave's tiles are done.
 //
 // Optionally the epilogue also emits each wave's top-m composite selection
 // keys (score, then lower block index) -- the candidate lists of the top-k.
@@ -48,8 +54,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Up to 64 indexer heads the register budget is held to two waves per SIMD;
+// more heads need more registers and run one wave per SIMD.
 template <int IHD, int MT>
-__global__ __launch_bounds__(256) void index_score_kernel(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2 : 1, 2))) void index_score_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint16_t* __restrict__ k_idx, int64_t k_rows,
     const int64_t* __restrict__ pos, const int64_t* __restrict__ seq_kv,
@@ -58,20 +66,66 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     uint32_t* __restrict__ nvalid, int cand_m, uint32_t* __restrict__ err,
     int tiles_per_wave) {
   constexpr int KS = IHD / 16;          // MFMA k-steps (one 16-byte chunk per lane each)
-  constexpr int CPR = IHD / 8;          // 16-byte chunks per key row
+  constexpr int CPR = IHD / 8;          // 16-byte chunks per key or query row
   constexpr int TILE_CHUNKS = kTileN * CPR;
   constexpr int LPT = TILE_CHUNKS / 64; // DMA instructions per tile (1 KiB each)
+  constexpr int QCHUNKS = MT * 32 * CPR;
+  // Up to 64 heads each wave keeps its query operands in VGPRs; with more,
+  // they are read from LDS at every k-step (two waves per SIMD leave no room).
+  constexpr bool kQRegs = MT <= 2;
+  static_assert(kWaves * 2 * TILE_CHUNKS * 16 + QCHUNKS * 16 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) u32x4 ktile[kWaves][2][TILE_CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4 qlds[QCHUNKS];
 
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
+  const uint16_t* qt = q_idx + (int64_t)t * n_ih * IHD;
+
+  // ---- one round trip: query block (to LDS), head weights, metadata ----
+  // Query chunk e = row*CPR + p of the padded head block goes to LDS slot e,
+  // holding global chunk p ^ (row % CPR); padded heads re-read the last real
+  // head (their weight is zero, so they add nothing).
+#pragma unroll
+  for (int e0 = 0; e0 < QCHUNKS; e0 += kWaves * 64) {
+    const int e = e0 + wave * 64 + lane;
+    if (e0 + wave * 64 < QCHUNKS) {  // wave-uniform
+      const int r = e / CPR, pp = e % CPR;
+      const int hq = r < n_ih ? r : n_ih - 1;
+      lds_dma16(qt + (int64_t)hq * IHD + (pp ^ (r & (CPR - 1))) * 8, &qlds[e0 + wave * 64]);
+    }
+  }
+  // A operand of k-step s for lane (col, half): q[head = mt*32+col][16*s +
+  // 8*half .. +8]; accumulator element r of lane (col, half) is head
+  // 8*(r/4) + 4*half + (r%4) of its 32-head tile.
+  auto q_operand = [&](int mt, int s) {
+    const int r = mt * 32 + col;
+    const int c = 2 * s + half;
+    return qlds[r * CPR + (c ^ (r & (CPR - 1)))];
+  };
+  float wv[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      wv[mt][r] = w[(int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1)];
+    }
+  }
+  // The token metadata and the scalar arguments are read in the same batch
+  // (the empty asm takes them as operands), rather than one dependent load
+  // after another as the branches below would otherwise order them.
+  const int64_t pos_t = pos[t];
+  const int32_t ncomp_t = n_comp[t];
+  const int64_t row0 = seq_kv[t];
+  asm volatile("" ::"s"(pos_t), "s"(ncomp_t), "s"(row0), "s"(k_rows), "s"(ld), "s"(ratio),
+               "s"(tiles_per_wave), "s"(n_ih));
+  wait_vmcnt<0>();  // query DMA and weight loads have landed
 
   uint32_t flags = 0;
-  int64_t n_vis = visible_count(pos[t], ratio, n_comp[t], &flags);
-  const int64_t row0 = seq_kv[t];
+  int64_t n_vis = visible_count(pos_t, ratio, ncomp_t, &flags);
   if (row0 < 0) {
     flags |= CSA_DERR_BAD_META;
     n_vis = 0;
@@ -84,51 +138,21 @@ __global__ __launch_bounds__(256) void index_score_kernel(
     n_vis = ld;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) report(err, flags);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (hw >= n_ih) wv[mt][r] = 0.0f;
+    }
+  }
 
   const int64_t n_tiles = (n_vis + kTileN - 1) / kTileN;
   const int64_t tile_begin = ((int64_t)blockIdx.x * kWaves + wave) * tiles_per_wave;
   const int64_t tile_end = min(tile_begin + (int64_t)tiles_per_wave, n_tiles);
   const int64_t wslot = (int64_t)t * gridDim.x * kWaves + (int64_t)blockIdx.x * kWaves + wave;
-  if (tile_begin >= tile_end) {  // wave-uniform; no workgroup barrier follows
-    if (cand != nullptr && lane == 0) {
-      nvalid[wslot] = 0u;
-      for (int i = 0; i < cand_m; ++i) cand[wslot * cand_m + i] = 0ull;
-    }
-    return;
-  }
+  const bool active = tile_begin < tile_end;  // wave-uniform
   const char* kbase = reinterpret_cast<const char*>(k_idx + row0 * IHD);
-
-  // A operand: lane (col, half) holds q[head = mt*32+col][16*s + 8*half .. +8]
-  // for k-step s; padded heads are zero.  Accumulator element r of lane
-  // (col, half) is head 8*(r/4) + 4*half + (r%4) of its 32-head tile.
-  u32x4 qv[MT][KS];
-  float wv[MT][16];
-  const uint16_t* qt = q_idx + (int64_t)t * n_ih * IHD;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int head = mt * 32 + col;
-    const int hq = head < n_ih ? head : n_ih - 1;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qt + (int64_t)hq * IHD + 16 * s + 8 * half);
-      qv[mt][s] = head < n_ih ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      const float x = w[(int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1)];
-      wv[mt][r] = hw < n_ih ? x : 0.0f;
-    }
-  }
-  // Settle those loads here: the loop then carries no pending register loads
-  // and its waits count tile DMAs only.
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : "+v"(qv[mt][s]));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wv[mt][r]));
-  }
 
   // DMA of one tile into buffer b: instruction i, lane l -> tile row
   // r = (i*64 + l) / CPR, LDS slot p = l % CPR, holding global chunk p ^ (r % CPR).
@@ -144,48 +168,66 @@ __global__ __launch_bounds__(256) void index_score_kernel(
       lds_dma16(kbase + blk * (IHD * 2) + c * 16, &ktile[wave][b][i * 64]);
     }
   };
-  issue_tile(tile_begin, 0);
-  if (tile_begin + 1 < tile_end) issue_tile(tile_begin + 1, 1);
+  if (active) {
+    issue_tile(tile_begin, 0);
+    if (tile_begin + 1 < tile_end) issue_tile(tile_begin + 1, 1);
+  }
+  __syncthreads();  // the query block is in LDS for every wave
+  if (!active) {
+    if (cand != nullptr && lane == 0) {
+      nvalid[wslot] = 0u;
+      for (int i = 0; i < cand_m; ++i) cand[wslot * cand_m + i] = 0ull;
+    }
+    return;
+  }
+  u32x4 qv[kQRegs ? MT : 1][KS];
+  if constexpr (kQRegs) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qv[mt][s] = q_operand(mt, s);
+  }
 
   float sc[kMaxTpw];
 #pragma unroll
-  for (int j = 0; j < kMaxTpw; ++j) sc[j] = 0.0f;
+  for (int j = 0; j < kMaxTpw; ++j) {
+    sc[j] = 0.0f;
+    const int64_t tile = tile_begin + j;
+    if (tile < tile_end) {  // wave-uniform
+      const int b = j & 1;
+      // all but the next tile's DMA (if issued) have landed
+      if (tile + 1 < tile_end) wait_vmcnt<LPT>(); else wait_vmcnt<0>();
+      u32x4 kb[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int c = 2 * s + half;
+        kb[s] = ktile[wave][b][col * CPR + (c ^ (col & (CPR - 1)))];
+      }
+      wait_lgkmcnt0();  // buffer b is free again
+      if (tile + 2 < tile_end) issue_tile(tile + 2, b);
 
-  int j = 0;
-  for (int64_t tile = tile_begin; tile < tile_end; ++tile, ++j) {
-    const int b = j & 1;
-    // all but the next tile's DMA (if issued) have landed
-    if (tile + 1 < tile_end) wait_vmcnt<LPT>(); else wait_vmcnt<0>();
-    u32x4 kb[KS];
+      f32x16 acc[MT];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int c = 2 * s + half;
-      kb[s] = ktile[wave][b][col * CPR + (c ^ (col & (CPR - 1)))];
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, kb[s]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const u32x4 qa = kQRegs ? qv[kQRegs ? mt : 0][s] : q_operand(mt, s);
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa), kv,
+                                                            acc[mt], 0, 0, 0);
+        }
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+      }
+      part += __shfl_xor(part, 32);
+      sc[j] = part;
     }
-    wait_lgkmcnt0();  // buffer b is free again
-    if (tile + 2 < tile_end) issue_tile(tile + 2, b);
-
-    f32x16 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kb[s]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qv[mt][s]),
-                                                          kv, acc[mt], 0, 0, 0);
-    }
-    float part = 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
-    }
-    part += __shfl_xor(part, 32);
-#pragma unroll
-    for (int q = 0; q < kMaxTpw; ++q)
-      if (q == j) sc[q] = part;
   }
 
   // coalesced score stores: lanes 0..31 hold consecutive blocks of each tile
@@ -198,21 +240,30 @@ __global__ __launch_bounds__(256) void index_score_kernel(
   }
 
   if (cand != nullptr) {
-    uint64_t key[kMaxTpw];
+    // both half-waves hold every tile's scores: half h takes tiles 2p + h
+    constexpr int KPL = kMaxTpw / 2;
+    float ks[KPL];
+    bool ok[KPL];
+    uint32_t blk[KPL];
 #pragma unroll
-    for (int q = 0; q < kMaxTpw; ++q) {
-      const int64_t blk = (tile_begin + q) * kTileN + col;
-      key[q] = (q < nt && half == 0 && blk < n_vis) ? block_key(sc[q], (uint32_t)blk) : 0ull;
+    for (int p = 0; p < KPL; ++p) {
+      const int q = 2 * p + half;
+      const int64_t b = (tile_begin + q) * kTileN + col;
+      float x0 = sc[2 * p], x1 = sc[2 * p + 1];
+      asm volatile("" : "+v"(x0), "+v"(x1));  // keep sc[] in registers: no indexed load
+      ks[p] = half ? x1 : x0;
+      ok[p] = q < nt && b < n_vis;
+      blk[p] = (uint32_t)b;
     }
-    wave_top_m<kMaxTpw>(key, cand_m, cand + wslot * cand_m);
-    if (lane == 0) nvalid[wslot] = (uint32_t)(min(n_vis, tile_end * kTileN) - tile_begin * kTileN);
+    const uint32_t n_ok = wave_top_m<KPL>(ks, ok, blk, (uint32_t)cand_m, cand + wslot * cand_m);
+    if (lane == 0) nvalid[wslot] = n_ok;
   }
 }
 
 template <int IHD, int MT>
 hipError_t launch_t(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t s) {
   dim3 grid(p.wgs_per_token, a.T);
-  hipLaunchKernelGGL((index_score_kernel<IHD, MT>), grid, dim3(256), 0, s, a.q_idx, a.w,
+  hipLaunchKernelGGL((index_score_kernel<IHD, MT>), grid, dim3(kWaves * 64), 0, s, a.q_idx, a.w,
                      a.k_idx, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.n_ih, a.ratio, a.scores,
                      a.ld, a.cand, a.nvalid, a.cand_m, a.err, p.tiles_per_wave);
   return hipGetLastError();
@@ -232,13 +283,13 @@ hipError_t launch_ihd(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t
 }  // namespace
 
 IndexPlan plan_index(int T, int64_t ld) {
-  // Every wave owns `tpw` consecutive 32-block tiles; about two resident
-  // workgroups per CU over the whole batch (256 CUs), at most kMaxTpw tiles
-  // per wave.
+  // Every wave owns `tpw` consecutive 32-block tiles; about one resident
+  // workgroup per CU (256 CUs x kWaves waves) over the whole batch, at most
+  // kMaxTpw tiles per wave.
   IndexPlan p;
   const int64_t tiles = (ld + kTileN - 1) / kTileN;
   const int64_t total = tiles * (T > 0 ? T : 1);
-  int64_t tpw = (total + kWaves * 512 - 1) / (kWaves * 512);
+  int64_t tpw = (total + kWaves * 256 - 1) / (kWaves * 256);
   if (tpw < 1) tpw = 1;
   if (tpw > kMaxTpw) tpw = kMaxTpw;
   p.tiles_per_wave = (int)tpw;

@@ -594,16 +594,22 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
   const int64_t wslot = (int64_t)t * gridDim.x * (kCandThreads / 64) + wg;
   const int64_t b0 = wg * blocks_per_wave;
   const int64_t b1 = min(b0 + (int64_t)blocks_per_wave, n_vis);
-  uint64_t key[KPL];
   const float* srow = scores + (int64_t)t * ld;
+  // half-wave h takes the 32-block pieces 2p + h of the group
+  constexpr int KPH = KPL / 2;
+  float sc[KPH];
+  bool ok[KPH];
+  uint32_t blk[KPH];
 #pragma unroll
-  for (int q = 0; q < KPL; ++q) {
-    const int64_t blk = b0 + q * 32 + (lane & 31);
-    key[q] = (lane < 32 && q * 32 < blocks_per_wave && blk < b1) ? block_key(srow[blk], (uint32_t)blk)
-                                                                  : 0ull;
+  for (int p = 0; p < KPH; ++p) {
+    const int piece = 2 * p + (lane >> 5);
+    const int64_t b = b0 + piece * 32 + (lane & 31);
+    ok[p] = piece * 32 < blocks_per_wave && b < b1;
+    blk[p] = (uint32_t)b;
+    sc[p] = ok[p] ? srow[b] : 0.0f;
   }
-  wave_top_m<KPL>(key, cand_m, cand + wslot * cand_m);
-  if (lane == 0) nvalid[wslot] = b1 > b0 ? (uint32_t)(b1 - b0) : 0u;
+  const uint32_t n_ok = wave_top_m<KPH>(sc, ok, blk, (uint32_t)cand_m, cand + wslot * cand_m);
+  if (lane == 0) nvalid[wslot] = n_ok;
 }
 
 }  // namespace
