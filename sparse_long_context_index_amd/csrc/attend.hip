@@ -6,21 +6,23 @@
 //
 // Split-K flash decoding on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16), with
 // the products transposed so that each lane owns one query head:
-//   * a workgroup = 4 waves = up to 64 query heads (16 per wave, one per lane
-//     column); the grid is (row splits, 64-head groups, tokens);
+//   * a workgroup = 4 waves serving 16 query heads (one per lane column) on a
+//     run of 64-row tiles; the grid is (row splits, 16-head groups, tokens),
+//     so a decode token's rows spread over many CUs while each workgroup
+//     fetches only its heads' queries and writes only their partials;
 //   * rows stream through LDS in 64-row tiles; each tile is staged twice from
 //     one set of 16-byte global loads: row-major (A operand of S^T = K Q^T) and
 //     8-row interleaved (A operand of O^T += V^T P^T), the latter transposed in
 //     registers with v_perm so that both products read 16 bytes per lane;
-//   * S^T leaves each lane 16 scores of its own head; the fp32 online softmax
-//     (exp2 domain) needs only two cross-lane steps, and P^T goes from those
-//     registers straight into the B operand of the second product, because the
-//     interleaved V^T groups are staged in the same row order (attention does
-//     not depend on the order of its rows);
-//   * O^T leaves each lane four consecutive d of its head, stored 16 bytes at
-//     a time: unnormalised partial outputs plus (max, sum) per split, merged by
-//     a small combine kernel (which also applies the sink).  With one split
-//     the workgroup writes the final output directly.
+//   * wave w computes S^T for tile rows 16w..16w+15; the fp32 online softmax
+//     (exp2 domain) combines the waves' row maxima and sums through LDS, and
+//     P is exchanged there in the row order of the interleaved V^T groups
+//     (attention does not depend on the order of its rows);
+//   * wave w then accumulates O^T for its quarter of head_dim; each lane holds
+//     four consecutive d of its head, stored 16 bytes at a time: unnormalised
+//     partial outputs plus (max, sum) per split, merged by a small combine
+//     kernel (which also applies the sink).  With one split the workgroup
+//     writes the final output directly.
 // The row set of token t is segment A followed by segment B, read in place, so
 // the HCA path needs no concatenation.  In the decode step the CSA rows are
 // gathered here (selected compressed rows through their block indices, then
@@ -32,7 +34,7 @@ namespace csa {
 namespace {
 
 constexpr int kRT = 64;          // rows per tile
-constexpr int kHeadsPerWg = 64;  // 4 waves x 16 heads
+constexpr int kHeadsPerWg = 16;  // query heads per workgroup (one per lane column)
 constexpr int kMaxSplits = 256;
 constexpr int64_t kSegB = 1ll << 62;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -109,10 +111,12 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
                                                            int n_splits) {
   using L = Layout<D>;
   constexpr int KSQ = D / 32;  // k-steps of S^T = K Q^T
-  constexpr int NTO = D / 16;  // 16-wide d tiles of O^T
+  constexpr int NTW = D / 64;  // 16-wide d tiles of O^T per wave (a quarter of D)
   constexpr int DP = D / 8;    // 16-byte pieces per row
   __shared__ __attribute__((aligned(16))) uint16_t rm[L::RM_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t il[L::IL_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t pl[kHeadsPerWg * kRT];  // P[head][tile row], bf16
+  __shared__ float red_m[4][kHeadsPerWg], red_l[4][kHeadsPerWg];
   __shared__ int64_t rsrc[kRT];  // element offset of each tile row (kSegB: segment B), -1: none
 
   const int t = blockIdx.z;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, quad = lane >> 4;
-  const int h = blockIdx.y * kHeadsPerWg + wave * 16 + li;  // this lane's query head
+  const int h = blockIdx.y * kHeadsPerWg + li;  // this lane's query head (every wave: the same 16)
 
   // Everything the first tile waits on is loaded up front: its selected block
   // indices (idx rows always hold sel_stride entries), Q, the row metadata.
@@ -149,11 +153,12 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int n_rows = sd.alen + sd.blen;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const float sl2 = p.scale * kLog2e;
+  const bool copy_rows = p.copy_out != nullptr && blockIdx.y == 0;
 
-  // o[n][r] = O^T[d = n*16 + 4*quad + r][head h] (unnormalised)
-  f32x4 o[NTO];
+  // o[nn][r] = O^T[d = (wave*NTW + nn)*16 + 4*quad + r][head h] (unnormalised)
+  f32x4 o[NTW];
 #pragma unroll
-  for (int n = 0; n < NTO; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NTW; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
   const uint16_t* kv_a = p.kv_a;
@@ -190,7 +195,8 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     // the order the S^T accumulators hold them, so 8-row group g = 4*kp + qg
     // is rows 32*kp + 16*(j/4) + 4*qg + j%4, j < 8.  Each thread loads one
     // 8x8 (rows x d) block of a group, writes it row-major (A operand of S^T)
-    // and transposed (A operand of O^T), and copies it to all_kv. ----
+    // and transposed (A operand of O^T), and (head group 0) copies it to
+    // all_kv. ----
     constexpr int NB = (kRT / 8) * DP;      // 8x8 blocks per tile
     constexpr int BPTH = (NB + 255) / 256;  // blocks per thread
     u32x4 rows[BPTH][8];
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
       for (int k = 0; k < 8; ++k) {
         const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
         *reinterpret_cast<u32x4*>(&rm[row * L::RM + dp * 8]) = rows[q][k];
-        if (p.copy_out != nullptr && r0 + row < row_end)
+        if (copy_rows && r0 + row < row_end)
           *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + r0 + row) * D +
                                     dp * 8) = rows[q][k];
       }
@@ -237,100 +243,86 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     }
     __syncthreads();
 
-    // ---- S^T = K Q^T for 64 rows x this wave's 16 heads.  The K fragments
-    // of k-step ks+1 are read from LDS while the MFMAs of ks run. ----
-    f32x4 s[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) s[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- S^T = K Q^T for this wave's 16 tile rows x the 16 heads.  The K
+    // fragments of k-step ks+1 are read from LDS while the MFMA of ks runs. ----
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      bf16x8 kb[2][4];
-      auto read_k = [&](int ks, bf16x8 (&dst)[4]) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          dst[nt] = *reinterpret_cast<const bf16x8*>(&rm[(nt * 16 + li) * L::RM + ks * 32 + quad * 8]);
-      };
-      read_k(0, kb[0]);
+      const uint16_t* krow = &rm[(wave * 16 + li) * L::RM + quad * 8];
+      bf16x8 kb[2];
+      kb[0] = *reinterpret_cast<const bf16x8*>(krow);
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) {
-        if (ks + 1 < KSQ) read_k(ks + 1, kb[(ks + 1) & 1]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1][nt], qa[ks], s[nt], 0, 0, 0);
+        if (ks + 1 < KSQ) kb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(krow + (ks + 1) * 32);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1], qa[ks], s, 0, 0, 0);
       }
     }
-    // s[nt][r] = S[head h][row r0 + nt*16 + 4*quad + r]
+    // s[r] = S[head h][tile row wave*16 + 4*quad + r]
 
-    // ---- online softmax (exp2 domain), one head per lane ----
-    float x[4][4];
+    // ---- online softmax (exp2 domain): per-wave maxima over 16 rows, then
+    // the tile maximum of each head through LDS ----
+    float x[4];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool valid = r0 + nt * 16 + 4 * quad + r < row_end;
-        x[nt][r] = valid ? s[nt][r] * sl2 : -INFINITY;
-        mloc = fmaxf(mloc, x[nt][r]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = r0 + wave * 16 + 4 * quad + r < row_end;
+      x[r] = valid ? s[r] * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, x[r]);
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float mnew = fmaxf(m_run, mloc);
+    if (quad == 0) red_m[wave][li] = mloc;
+    __syncthreads();
+    const float mtile = fmaxf(fmaxf(red_m[0][li], red_m[1][li]), fmaxf(red_m[2][li], red_m[3][li]));
+    const float mnew = fmaxf(m_run, mtile);
     const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run - mnew);
     float lsum = 0.f;
-    // P^T (B operand of O^T): k-step kp takes tiles 2kp, 2kp+1 of this lane
-    bf16x8 pb[2];
+    float pv[4];
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      uint32_t w[4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float xv = x[2 * kp + hh][r];
-          pv[r] = (xv == -INFINITY) ? 0.f : exp2f(xv - mnew);
-          lsum += pv[r];
-        }
-        w[2 * hh + 0] = (uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16);
-        w[2 * hh + 1] = (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16);
-      }
-      pb[kp] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = (x[r] == -INFINITY) ? 0.f : exp2f(x[r] - mnew);
+      lsum += pv[r];
     }
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * alpha + lsum;
+    // P[head li][tile rows wave*16 + 4*quad .. +4] as bf16
+    *reinterpret_cast<uint2*>(&pl[li * kRT + wave * 16 + 4 * quad]) =
+        make_uint2((uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16),
+                   (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16));
+    if (quad == 0) red_l[wave][li] = lsum;
+    __syncthreads();
+    l_run = l_run * alpha + (red_l[0][li] + red_l[1][li] + red_l[2][li] + red_l[3][li]);
     m_run = mnew;
 #pragma unroll
-    for (int n = 0; n < NTO; ++n) o[n] *= alpha;
+    for (int n = 0; n < NTW; ++n) o[n] *= alpha;
+    // P^T (B operand of O^T) for k-step kp: rows 32kp + 4*quad + 0..3 and
+    // 32kp + 16 + 4*quad + 0..3 of head li
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(&pl[li * kRT + 32 * kp + 4 * quad]);
+      const uint2 hi = *reinterpret_cast<const uint2*>(&pl[li * kRT + 32 * kp + 16 + 4 * quad]);
+      pb[kp] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
 
-    // ---- O^T += V^T P^T; V^T fragments are read four d-tiles ahead ----
-    {
-      constexpr int NS = 2 * NTO;  // (kp, n) steps
-      constexpr int GB = 4;        // fragments per batch
-      bf16x8 vb[2][GB];
-      auto read_v = [&](int b, bf16x8 (&dst)[GB]) {
+    // ---- O^T += V^T P^T for this wave's quarter of D ----
 #pragma unroll
-        for (int u = 0; u < GB; ++u) {
-          const int st = b * GB + u, kp = st / NTO, n = st - kp * NTO;
-          const int d = n * 16 + li;
-          dst[u] = *reinterpret_cast<const bf16x8*>(&il[(kp * 4 + quad) * L::ILG + d * 8 + (d >> 3) * 8]);
-        }
-      };
-      read_v(0, vb[0]);
+    for (int kp = 0; kp < kRT / 32; ++kp) {
+      const uint16_t* ilg = &il[(kp * 4 + quad) * L::ILG];
+      bf16x8 vb[NTW];
 #pragma unroll
-      for (int b = 0; b < NS / GB; ++b) {
-        if (b + 1 < NS / GB) read_v(b + 1, vb[(b + 1) & 1]);
-#pragma unroll
-        for (int u = 0; u < GB; ++u) {
-          const int st = b * GB + u, kp = st / NTO, n = st - kp * NTO;
-          o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[b & 1][u], pb[kp], o[n], 0, 0, 0);
-        }
+      for (int nn = 0; nn < NTW; ++nn) {
+        const int d = (wave * NTW + nn) * 16 + li;
+        vb[nn] = *reinterpret_cast<const bf16x8*>(ilg + d * 8 + (d >> 3) * 8);
       }
+#pragma unroll
+      for (int nn = 0; nn < NTW; ++nn)
+        o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[nn], pb[kp], o[nn], 0, 0, 0);
     }
   }
 
   report(p.err, flags);
-  // ---- epilogue: lane (li, quad) holds d = n*16 + 4*quad + r of head h ----
+  // ---- epilogue: lane (li, quad) of wave w holds d = (w*NTW + nn)*16 +
+  // 4*quad + r of head h ----
   if (h >= p.n_heads) return;
   if (n_splits == 1) {
     float M = m_run;
@@ -346,12 +338,12 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     const float inv = Lsum > 0.f ? f / Lsum : 0.f;
     uint16_t* oh = p.out + ((int64_t)t * p.n_heads + h) * D + 4 * quad;
 #pragma unroll
-    for (int n = 0; n < NTO; ++n) {
-      const uint32_t lo = (uint32_t)f32_to_bf16(o[n][0] * inv) | ((uint32_t)f32_to_bf16(o[n][1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(o[n][2] * inv) | ((uint32_t)f32_to_bf16(o[n][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(oh + n * 16) = make_uint2(lo, hi);
+    for (int nn = 0; nn < NTW; ++nn) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(o[nn][0] * inv) | ((uint32_t)f32_to_bf16(o[nn][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(o[nn][2] * inv) | ((uint32_t)f32_to_bf16(o[nn][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(oh + (wave * NTW + nn) * 16) = make_uint2(lo, hi);
     }
-    if (p.lse != nullptr && quad == 0)
+    if (p.lse != nullptr && wave == 0 && quad == 0)
       p.lse[(int64_t)t * p.n_heads + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
   } else {
     float* part_o = static_cast<float*>(p.ws);
@@ -359,8 +351,8 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     const size_t slot = ((size_t)t * n_splits + split) * p.n_heads + h;
     float* po = part_o + slot * D + 4 * quad;
 #pragma unroll
-    for (int n = 0; n < NTO; ++n) *reinterpret_cast<f32x4*>(po + n * 16) = o[n];
-    if (quad == 0) {
+    for (int nn = 0; nn < NTW; ++nn) *reinterpret_cast<f32x4*>(po + (wave * NTW + nn) * 16) = o[nn];
+    if (wave == 0 && quad == 0) {
       part_ml[slot * 2 + 0] = m_run;
       part_ml[slot * 2 + 1] = l_run;
     }
