@@ -48,30 +48,56 @@ struct Layout {
   static constexpr int IL_ELEMS = (kRT / 8) * ILG;
 };
 
+// Row-set mode of segment A (a template parameter of the split kernel, so
+// that the token metadata loads are unconditional and go out together).
+enum : int { kModeExplicit = 0, kModeVisible = 1, kModeGather = 2 };
+
 struct SegDesc {
   int64_t a0, b0;
   int alen, blen;
 };
 
-// Row set of token t.  Gather mode (p.sel_idx != nullptr): segment A is the
-// selected compressed rows comp_kv[seq_kv[t] + sel_idx[t, j]], j < sel_cnt[t],
-// segment B the SWA rows; the rows are also copied into all_kv while staged.
-__device__ SegDesc token_rows(const AttendLaunch& p, int t, uint32_t& flags) {
+// Per-token row metadata of the mode, read in one batch.
+struct TokMeta {
+  int64_t a_row0, vis_pos, b_row0;
+  int32_t a_cnt, vis_ncomp, b_len;
+};
+template <int MODE, bool HAS_B>
+__device__ __forceinline__ TokMeta load_meta(const AttendLaunch& p, int t) {
+  TokMeta m{};
+  m.a_row0 = p.a_row0 != nullptr ? p.a_row0[t] : (int64_t)t * p.a_stride;
+  if constexpr (MODE == kModeGather) m.a_cnt = p.sel_cnt[t];
+  if constexpr (MODE == kModeExplicit) m.a_cnt = p.a_len[t];
+  if constexpr (MODE == kModeVisible) {
+    m.vis_pos = p.vis_pos[t];
+    m.vis_ncomp = p.vis_ncomp[t];
+  }
+  if constexpr (HAS_B) {
+    m.b_row0 = p.b_row0[t];
+    m.b_len = p.b_len[t];
+  }
+  return m;
+}
+
+// Row set of token t.  Gather mode: segment A is the selected compressed rows
+// comp_kv[seq_kv[t] + sel_idx[t, j]], j < sel_cnt[t], segment B the SWA rows;
+// the rows are also copied into all_kv while staged.
+template <int MODE, bool HAS_B>
+__device__ SegDesc token_rows(const AttendLaunch& p, const TokMeta& m, uint32_t& flags) {
   SegDesc s;
   int64_t alen;
-  if (p.sel_idx != nullptr) {
-    s.a0 = p.a_row0[t];  // seq_kv
-    alen = p.sel_cnt[t];
+  s.a0 = m.a_row0;
+  if constexpr (MODE == kModeGather) {
+    alen = m.a_cnt;
     if (alen < 0 || alen > p.sel_stride) {
       flags |= CSA_DERR_COUNT_RANGE;
       alen = alen < 0 ? 0 : p.sel_stride;
     }
   } else {
-    s.a0 = p.a_row0 != nullptr ? p.a_row0[t] : (int64_t)t * p.a_stride;
-    if (p.vis_pos != nullptr) {
-      alen = visible_count(p.vis_pos[t], p.vis_ratio, p.vis_ncomp[t], &flags);
+    if constexpr (MODE == kModeVisible) {
+      alen = visible_count(m.vis_pos, p.vis_ratio, m.vis_ncomp, &flags);
     } else {
-      alen = p.a_len[t];
+      alen = m.a_cnt;
     }
     if (s.a0 < 0 || alen < 0 || s.a0 + alen > p.a_rows) {
       flags |= CSA_DERR_ROW_RANGE;
@@ -80,10 +106,10 @@ __device__ SegDesc token_rows(const AttendLaunch& p, int t, uint32_t& flags) {
   }
   int64_t blen = 0;
   s.b0 = 0;
-  if (p.kv_b != nullptr) {
-    s.b0 = p.b_row0[t];
-    blen = p.b_len[t];
-    if (p.sel_idx != nullptr && blen > p.b_cap) {
+  if constexpr (HAS_B) {
+    s.b0 = m.b_row0;
+    blen = m.b_len;
+    if (MODE == kModeGather && blen > p.b_cap) {
       flags |= CSA_DERR_COUNT_RANGE;
       blen = p.b_cap;
     }
@@ -106,9 +132,10 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint3
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
-template <int D>
+template <int D, int MODE, bool HAS_B>
 __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int tiles_per_split,
                                                            int n_splits) {
+  constexpr bool kGather = MODE == kModeGather;
   using L = Layout<D>;
   constexpr int KSQ = D / 32;  // k-steps of S^T = K Q^T
   constexpr int NTW = D / 64;  // 16-wide d tiles of O^T per wave (a quarter of D)
@@ -130,21 +157,22 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   // indices (idx rows always hold sel_stride entries), Q, the row metadata.
   int32_t pidx = 0;
   const int row_begin = split * tiles_per_split * kRT;
-  if (p.sel_idx != nullptr && tid < kRT)
+  if (kGather && tid < kRT)
     pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(row_begin + tid, p.sel_stride - 1)];
   // Q as the B operand of S^T = K Q^T: lane holds Q[h][ks*32 + quad*8 .. +8].
+  // A lane beyond n_heads computes with the last real head's query; its own
+  // results are never stored, and the softmax statistics are per head.
   bf16x8 qa[KSQ];
   {
-    const uint16_t* qh = p.q + ((int64_t)t * p.n_heads + h) * D + quad * 8;
+    const int hq = h < p.n_heads ? h : p.n_heads - 1;
+    const uint16_t* qh = p.q + ((int64_t)t * p.n_heads + hq) * D + quad * 8;
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (h < p.n_heads) v = *reinterpret_cast<const u32x4*>(qh + ks * 32);
-      qa[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ks = 0; ks < KSQ; ++ks)
+      qa[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + ks * 32));
   }
+  const TokMeta meta = load_meta<MODE, HAS_B>(p, t);
   uint32_t flags = 0;
-  const SegDesc sd = token_rows(p, t, flags);
+  const SegDesc sd = token_rows<MODE, HAS_B>(p, meta, flags);
   if (split == 0 && blockIdx.y == 0 && tid == 0) {
     report(p.err, flags);
     if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
@@ -153,7 +181,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int n_rows = sd.alen + sd.blen;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const float sl2 = p.scale * kLog2e;
-  const bool copy_rows = p.copy_out != nullptr && blockIdx.y == 0;
+  const bool copy_rows = kGather && p.copy_out != nullptr && blockIdx.y == 0;
 
   // o[nn][r] = O^T[d = (wave*NTW + nn)*16 + 4*quad + r][head h] (unnormalised)
   f32x4 o[NTW];
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
       if (rr < row_end) {
         if (rr < sd.alen) {
           int64_t ar = sd.a0 + rr;
-          if (p.sel_idx != nullptr) {
+          if constexpr (kGather) {
             ar = sd.a0 + pidx;
             if (ar < 0 || ar >= p.a_rows) {
               flags |= CSA_DERR_ROW_RANGE;
@@ -187,7 +215,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
       }
       rsrc[tid] = src;
       // prefetch the next tile's block indices
-      if (p.sel_idx != nullptr && r0 + kRT < row_end)
+      if (kGather && r0 + kRT < row_end)
         pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(r0 + kRT + tid, p.sel_stride - 1)];
     }
     __syncthreads();
@@ -478,8 +506,20 @@ hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
   const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
   const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
   dim3 grid((unsigned)sp.n_splits, (unsigned)n_hg, (unsigned)a.T);
-  hipLaunchKernelGGL((attend_split_kernel<D>), grid, dim3(256), 0, s, a, sp.tiles_per_split,
-                     sp.n_splits);
+  const int mode = a.sel_idx != nullptr ? kModeGather
+                   : a.vis_pos != nullptr ? kModeVisible
+                                          : kModeExplicit;
+#define CSA_SPLIT(MODE, HB)                                                                  \
+  hipLaunchKernelGGL((attend_split_kernel<D, MODE, HB>), grid, dim3(256), 0, s, a,          \
+                     sp.tiles_per_split, sp.n_splits)
+  if (mode == kModeGather) {
+    if (a.kv_b != nullptr) CSA_SPLIT(kModeGather, true); else CSA_SPLIT(kModeGather, false);
+  } else if (mode == kModeVisible) {
+    if (a.kv_b != nullptr) CSA_SPLIT(kModeVisible, true); else CSA_SPLIT(kModeVisible, false);
+  } else {
+    if (a.kv_b != nullptr) CSA_SPLIT(kModeExplicit, true); else CSA_SPLIT(kModeExplicit, false);
+  }
+#undef CSA_SPLIT
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.n_splits == 1) return e;
   hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),
