@@ -87,7 +87,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+              "sharding the path over several GPUs is not built", file=sys.stderr)
         return 2
 
     import numpy as np

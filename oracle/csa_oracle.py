@@ -24,7 +24,7 @@ Sources (web pages of the ``nvfp4-megamoe-kernel`` design notes):
   compressed blocks strictly before its own, incomplete block; the newest
   tokens are attended both in SWA and in the newest compressed block).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * visible blocks of a query at 0-based position ``pos`` = ``floor(pos/ratio)``,
   capped by the blocks stored for its sequence;

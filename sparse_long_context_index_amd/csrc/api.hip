@@ -271,7 +271,8 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   const TopkPlan tp = plan_topk(a->T, a->max_vis, a->top_k);
   const TopkWs tw = topk_ws_layout(base + lay.topk, a->T, tp);
 
-  // S1 (+ per-wave candidate lists) -> S2 -> S3 fused into S4.
+  // S1 (+ per-wave candidate lists), then S2 with S3 fused into S4: one
+  // select-and-attend kernel for small batches, else top-k then attention.
   IndexScoreLaunch I{};
   I.q_idx = a->q_idx; I.w = a->w; I.k_idx = a->k_idx; I.k_rows = a->k_rows;
   I.pos = a->pos; I.seq_kv = a->seq_kv; I.n_comp = a->n_comp;
@@ -279,18 +280,26 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   I.scores = scores; I.ld = a->max_vis;
   I.cand = tw.cand; I.nvalid = tw.nvalid; I.cand_m = tp.cand_m; I.err = a->err;
   hipError_t e = launch_index_score(I, st);
-  if (e == hipSuccess)
+  if (e != hipSuccess) return hip_status(e);
+  L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
+  L.a_stride = 0; L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
+  L.sel_idx = idx; L.sel_cnt = count; L.sel_stride = a->top_k;
+  L.kv_b = a->swa; L.b_rows = a->swa_rows; L.b_row0 = a->swa_row0; L.b_len = a->swa_len;
+  L.b_cap = a->window;
+  L.copy_out = a->all_kv; L.copy_stride = a->top_k + a->window; L.n_kv_out = n_kv;
+  L.max_rows = a->top_k + a->window;
+  if (select_attend_fits(a->T, a->n_heads, L.max_rows)) {
+    SelectLaunch S{};
+    S.scores = scores; S.ld = a->max_vis; S.pos = a->pos; S.n_comp = a->n_comp;
+    S.ratio = a->ratio; S.top_k = a->top_k;
+    S.cand = tw.cand; S.nvalid = tw.nvalid; S.waves_per_token = tp.waves_per_token;
+    S.blocks_per_wave = tp.blocks_per_wave; S.cand_m = tp.cand_m;
+    S.idx = idx; S.count = count;
+    e = launch_select_attend(S, L, st);
+  } else {
     e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->T, a->ratio, a->top_k, tp,
                            tw, idx, count, a->err, st);
-  if (e == hipSuccess) {
-    L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
-    L.a_stride = 0; L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
-    L.sel_idx = idx; L.sel_cnt = count; L.sel_stride = a->top_k;
-    L.kv_b = a->swa; L.b_rows = a->swa_rows; L.b_row0 = a->swa_row0; L.b_len = a->swa_len;
-    L.b_cap = a->window;
-    L.copy_out = a->all_kv; L.copy_stride = a->top_k + a->window; L.n_kv_out = n_kv;
-    L.max_rows = a->top_k + a->window;
-    e = launch_attend(L, st);
+    if (e == hipSuccess) e = launch_attend(L, st);
   }
   return hip_status(e);
 }

@@ -28,7 +28,7 @@
 // gathered here (selected compressed rows through their block indices, then
 // the SWA rows) and copied into all_kv while they are staged, which fuses the
 // gather stage into the attention.
-#include "csa_common.h"
+#include "select_core.h"
 
 namespace csa {
 namespace {
@@ -83,7 +83,7 @@ __device__ __forceinline__ TokMeta load_meta(const AttendLaunch& p, int t) {
 // comp_kv[seq_kv[t] + sel_idx[t, j]], j < sel_cnt[t], segment B the SWA rows;
 // the rows are also copied into all_kv while staged.
 template <int MODE, bool HAS_B>
-__device__ SegDesc token_rows(const AttendLaunch& p, const TokMeta& m, uint32_t& flags) {
+__device__ __forceinline__ SegDesc token_rows(const AttendLaunch& p, const TokMeta& m, uint32_t& flags) {
   SegDesc s;
   int64_t alen;
   s.a0 = m.a_row0;
@@ -132,56 +132,41 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint3
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
-template <int D, int MODE, bool HAS_B>
-__global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int tiles_per_split,
-                                                           int n_splits) {
+// LDS of the tile loop (the fused kernel overlays it on the select's LDS).
+template <int D>
+struct alignas(16) AttSmem {
+  using L = Layout<D>;
+  uint16_t rm[L::RM_ELEMS];              // tile, row-major
+  uint16_t il[L::IL_ELEMS];              // tile, 8-row groups transposed
+  uint16_t pl[kHeadsPerWg * kRT];        // P[head][tile row], bf16
+  float red_m[4][kHeadsPerWg], red_l[4][kHeadsPerWg];
+  int64_t rsrc[kRT];  // element offset of each tile row (kSegB: segment B), -1: none
+};
+
+// The tile loop and epilogue of one workgroup: rows [row_begin, row_end) of
+// token t for the 16 heads of blockIdx.y.  NT threads stage the tiles; waves
+// 0-3 run the products and the softmax (the others only join the barriers).
+// Q comes from registers (qa) or from LDS (qlds, 16 rows of D+8); in gather
+// mode the block index of row rr comes from a prefetch of sel_idx (pidx holds
+// the first tile's) or, when SEL_LDS, from selrow[rr - row_begin].
+template <int D, int MODE, bool HAS_B, int NT, bool Q_LDS, bool SEL_LDS>
+__device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& sm, int t,
+                                             int split, int n_splits, int row_begin, int row_end,
+                                             const SegDesc& sd, int32_t pidx,
+                                             const int32_t* selrow, const bf16x8 (&qa)[D / 32],
+                                             const uint16_t* qlds, bool copy_rows) {
   constexpr bool kGather = MODE == kModeGather;
   using L = Layout<D>;
   constexpr int KSQ = D / 32;  // k-steps of S^T = K Q^T
   constexpr int NTW = D / 64;  // 16-wide d tiles of O^T per wave (a quarter of D)
   constexpr int DP = D / 8;    // 16-byte pieces per row
-  __shared__ __attribute__((aligned(16))) uint16_t rm[L::RM_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t il[L::IL_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[kHeadsPerWg * kRT];  // P[head][tile row], bf16
-  __shared__ float red_m[4][kHeadsPerWg], red_l[4][kHeadsPerWg];
-  __shared__ int64_t rsrc[kRT];  // element offset of each tile row (kSegB: segment B), -1: none
-
-  const int t = blockIdx.z;
-  const int split = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, quad = lane >> 4;
-  const int h = blockIdx.y * kHeadsPerWg + li;  // this lane's query head (every wave: the same 16)
-
-  // Everything the first tile waits on is loaded up front: its selected block
-  // indices (idx rows always hold sel_stride entries), Q, the row metadata.
-  int32_t pidx = 0;
-  const int row_begin = split * tiles_per_split * kRT;
-  if (kGather && tid < kRT)
-    pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(row_begin + tid, p.sel_stride - 1)];
-  // Q as the B operand of S^T = K Q^T: lane holds Q[h][ks*32 + quad*8 .. +8].
-  // A lane beyond n_heads computes with the last real head's query; its own
-  // results are never stored, and the softmax statistics are per head.
-  bf16x8 qa[KSQ];
-  {
-    const int hq = h < p.n_heads ? h : p.n_heads - 1;
-    const uint16_t* qh = p.q + ((int64_t)t * p.n_heads + hq) * D + quad * 8;
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks)
-      qa[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + ks * 32));
-  }
-  const TokMeta meta = load_meta<MODE, HAS_B>(p, t);
+  const bool mma = NT == 256 || wave < 4;       // waves of the products
+  const int h = blockIdx.y * kHeadsPerWg + li;  // this lane's query head
   uint32_t flags = 0;
-  const SegDesc sd = token_rows<MODE, HAS_B>(p, meta, flags);
-  if (split == 0 && blockIdx.y == 0 && tid == 0) {
-    report(p.err, flags);
-    if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
-  }
-  flags = 0;
-  const int n_rows = sd.alen + sd.blen;
-  const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const float sl2 = p.scale * kLog2e;
-  const bool copy_rows = kGather && p.copy_out != nullptr && blockIdx.y == 0;
 
   // o[nn][r] = O^T[d = (wave*NTW + nn)*16 + 4*quad + r][head h] (unnormalised)
   f32x4 o[NTW];
@@ -202,7 +187,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
         if (rr < sd.alen) {
           int64_t ar = sd.a0 + rr;
           if constexpr (kGather) {
-            ar = sd.a0 + pidx;
+            ar = sd.a0 + (SEL_LDS ? selrow[rr - row_begin] : pidx);
             if (ar < 0 || ar >= p.a_rows) {
               flags |= CSA_DERR_ROW_RANGE;
               ar = -1;
@@ -213,9 +198,9 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
           src = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
         }
       }
-      rsrc[tid] = src;
+      sm.rsrc[tid] = src;
       // prefetch the next tile's block indices
-      if (kGather && r0 + kRT < row_end)
+      if (kGather && !SEL_LDS && r0 + kRT < row_end)
         pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(r0 + kRT + tid, p.sel_stride - 1)];
     }
     __syncthreads();
@@ -225,17 +210,17 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     // 8x8 (rows x d) block of a group, writes it row-major (A operand of S^T)
     // and transposed (A operand of O^T), and (head group 0) copies it to
     // all_kv. ----
-    constexpr int NB = (kRT / 8) * DP;      // 8x8 blocks per tile
-    constexpr int BPTH = (NB + 255) / 256;  // blocks per thread
+    constexpr int NB = (kRT / 8) * DP;     // 8x8 blocks per tile
+    constexpr int BPTH = (NB + NT - 1) / NT;  // blocks per thread
     u32x4 rows[BPTH][8];
 #pragma unroll
     for (int q = 0; q < BPTH; ++q) {
-      const int b = tid + q * 256;
+      const int b = tid + q * NT;
       const int g = b / DP, dp = b - g * DP;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
-        const int64_t src = b < NB ? rsrc[row] : -1;
+        const int64_t src = b < NB ? sm.rsrc[row] : -1;
         rows[q][k] = u32x4{0u, 0u, 0u, 0u};
         if (src >= 0) {
           const uint16_t* base = (src & kSegB) ? kv_b : kv_a;
@@ -245,18 +230,18 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     }
 #pragma unroll
     for (int q = 0; q < BPTH; ++q) {
-      const int b = tid + q * 256;
+      const int b = tid + q * NT;
       if (b >= NB) break;
       const int g = b / DP, dp = b - g * DP;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
-        *reinterpret_cast<u32x4*>(&rm[row * L::RM + dp * 8]) = rows[q][k];
+        *reinterpret_cast<u32x4*>(&sm.rm[row * L::RM + dp * 8]) = rows[q][k];
         if (copy_rows && r0 + row < row_end)
           *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + r0 + row) * D +
                                     dp * 8) = rows[q][k];
       }
-      uint16_t* ilg = &il[g * L::ILG + dp * 8 * 8 + dp * 8];
+      uint16_t* ilg = &sm.il[g * L::ILG + dp * 8 * 8 + dp * 8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
@@ -271,87 +256,99 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
     }
     __syncthreads();
 
-    // ---- S^T = K Q^T for this wave's 16 tile rows x the 16 heads.  The K
-    // fragments of k-step ks+1 are read from LDS while the MFMA of ks runs. ----
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t* krow = &rm[(wave * 16 + li) * L::RM + quad * 8];
-      bf16x8 kb[2];
+    float x[4];
+    if (mma) {
+      // ---- S^T = K Q^T for this wave's 16 tile rows x the 16 heads.  The
+      // fragments of k-step ks+1 are read from LDS while the MFMA of ks runs.
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = &sm.rm[(wave * 16 + li) * L::RM + quad * 8];
+      const uint16_t* qrow = qlds + li * (D + 8) + quad * 8;
+      bf16x8 kb[2], qb[2];
       kb[0] = *reinterpret_cast<const bf16x8*>(krow);
+      if constexpr (Q_LDS) qb[0] = *reinterpret_cast<const bf16x8*>(qrow);
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) {
-        if (ks + 1 < KSQ) kb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(krow + (ks + 1) * 32);
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1], qa[ks], s, 0, 0, 0);
+        if (ks + 1 < KSQ) {
+          kb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(krow + (ks + 1) * 32);
+          if constexpr (Q_LDS) qb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(qrow + (ks + 1) * 32);
+        }
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1], Q_LDS ? qb[ks & 1] : qa[ks], s, 0,
+                                                    0, 0);
       }
-    }
-    // s[r] = S[head h][tile row wave*16 + 4*quad + r]
-
-    // ---- online softmax (exp2 domain): per-wave maxima over 16 rows, then
-    // the tile maximum of each head through LDS ----
-    float x[4];
-    float mloc = -INFINITY;
+      // s[r] = S[head h][tile row wave*16 + 4*quad + r]
+      // ---- online softmax (exp2 domain): per-wave maxima over 16 rows, then
+      // the tile maximum of each head through LDS ----
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool valid = r0 + wave * 16 + 4 * quad + r < row_end;
-      x[r] = valid ? s[r] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, x[r]);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    if (quad == 0) red_m[wave][li] = mloc;
-    __syncthreads();
-    const float mtile = fmaxf(fmaxf(red_m[0][li], red_m[1][li]), fmaxf(red_m[2][li], red_m[3][li]));
-    const float mnew = fmaxf(m_run, mtile);
-    const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run - mnew);
-    float lsum = 0.f;
-    float pv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pv[r] = (x[r] == -INFINITY) ? 0.f : exp2f(x[r] - mnew);
-      lsum += pv[r];
-    }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    // P[head li][tile rows wave*16 + 4*quad .. +4] as bf16
-    *reinterpret_cast<uint2*>(&pl[li * kRT + wave * 16 + 4 * quad]) =
-        make_uint2((uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16),
-                   (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16));
-    if (quad == 0) red_l[wave][li] = lsum;
-    __syncthreads();
-    l_run = l_run * alpha + (red_l[0][li] + red_l[1][li] + red_l[2][li] + red_l[3][li]);
-    m_run = mnew;
-#pragma unroll
-    for (int n = 0; n < NTW; ++n) o[n] *= alpha;
-    // P^T (B operand of O^T) for k-step kp: rows 32kp + 4*quad + 0..3 and
-    // 32kp + 16 + 4*quad + 0..3 of head li
-    bf16x8 pb[2];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(&pl[li * kRT + 32 * kp + 4 * quad]);
-      const uint2 hi = *reinterpret_cast<const uint2*>(&pl[li * kRT + 32 * kp + 16 + 4 * quad]);
-      pb[kp] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-    }
-
-    // ---- O^T += V^T P^T for this wave's quarter of D ----
-#pragma unroll
-    for (int kp = 0; kp < kRT / 32; ++kp) {
-      const uint16_t* ilg = &il[(kp * 4 + quad) * L::ILG];
-      bf16x8 vb[NTW];
-#pragma unroll
-      for (int nn = 0; nn < NTW; ++nn) {
-        const int d = (wave * NTW + nn) * 16 + li;
-        vb[nn] = *reinterpret_cast<const bf16x8*>(ilg + d * 8 + (d >> 3) * 8);
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = r0 + wave * 16 + 4 * quad + r < row_end;
+        x[r] = valid ? s[r] * sl2 : -INFINITY;
+        mloc = fmaxf(mloc, x[r]);
       }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      if (quad == 0) sm.red_m[wave][li] = mloc;
+    }
+    __syncthreads();
+    float alpha = 1.f;
+    if (mma) {
+      const float mtile = fmaxf(fmaxf(sm.red_m[0][li], sm.red_m[1][li]),
+                                fmaxf(sm.red_m[2][li], sm.red_m[3][li]));
+      const float mnew = fmaxf(m_run, mtile);
+      alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run - mnew);
+      float lsum = 0.f;
+      float pv[4];
 #pragma unroll
-      for (int nn = 0; nn < NTW; ++nn)
-        o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[nn], pb[kp], o[nn], 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        pv[r] = (x[r] == -INFINITY) ? 0.f : exp2f(x[r] - mnew);
+        lsum += pv[r];
+      }
+      lsum += __shfl_xor(lsum, 16);
+      lsum += __shfl_xor(lsum, 32);
+      // P[head li][tile rows wave*16 + 4*quad .. +4] as bf16
+      *reinterpret_cast<uint2*>(&sm.pl[li * kRT + wave * 16 + 4 * quad]) =
+          make_uint2((uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16),
+                     (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16));
+      if (quad == 0) sm.red_l[wave][li] = lsum;
+      m_run = mnew;
+    }
+    __syncthreads();
+    if (mma) {
+      l_run = l_run * alpha +
+              (sm.red_l[0][li] + sm.red_l[1][li] + sm.red_l[2][li] + sm.red_l[3][li]);
+#pragma unroll
+      for (int n = 0; n < NTW; ++n) o[n] *= alpha;
+      // P^T (B operand of O^T) for k-step kp: rows 32kp + 4*quad + 0..3 and
+      // 32kp + 16 + 4*quad + 0..3 of head li
+      bf16x8 pb[2];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(&sm.pl[li * kRT + 32 * kp + 4 * quad]);
+        const uint2 hi =
+            *reinterpret_cast<const uint2*>(&sm.pl[li * kRT + 32 * kp + 16 + 4 * quad]);
+        pb[kp] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      }
+      // ---- O^T += V^T P^T for this wave's quarter of D ----
+#pragma unroll
+      for (int kp = 0; kp < kRT / 32; ++kp) {
+        const uint16_t* ilg = &sm.il[(kp * 4 + quad) * L::ILG];
+        bf16x8 vb[NTW];
+#pragma unroll
+        for (int nn = 0; nn < NTW; ++nn) {
+          const int d = (wave * NTW + nn) * 16 + li;
+          vb[nn] = *reinterpret_cast<const bf16x8*>(ilg + d * 8 + (d >> 3) * 8);
+        }
+#pragma unroll
+        for (int nn = 0; nn < NTW; ++nn)
+          o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[nn], pb[kp], o[nn], 0, 0, 0);
+      }
     }
   }
 
   report(p.err, flags);
   // ---- epilogue: lane (li, quad) of wave w holds d = (w*NTW + nn)*16 +
   // 4*quad + r of head h ----
-  if (h >= p.n_heads) return;
+  if (!mma || h >= p.n_heads) return;
   if (n_splits == 1) {
     float M = m_run;
     float Lsum = l_run;
@@ -385,6 +382,134 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
       part_ml[slot * 2 + 1] = l_run;
     }
   }
+}
+
+template <int D, int MODE, bool HAS_B>
+__global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int tiles_per_split,
+                                                           int n_splits) {
+  constexpr bool kGather = MODE == kModeGather;
+  constexpr int KSQ = D / 32;
+  __shared__ AttSmem<D> sm;
+  const int t = blockIdx.z;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int li = lane & 15, quad = lane >> 4;
+  const int h = blockIdx.y * kHeadsPerWg + li;
+
+  // Everything the first tile waits on is loaded up front: its selected block
+  // indices (idx rows always hold sel_stride entries), Q, the row metadata.
+  int32_t pidx = 0;
+  const int row_begin = split * tiles_per_split * kRT;
+  if (kGather && tid < kRT)
+    pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(row_begin + tid, p.sel_stride - 1)];
+  // Q as the B operand of S^T = K Q^T: lane holds Q[h][ks*32 + quad*8 .. +8].
+  // A lane beyond n_heads computes with the last real head's query; its own
+  // results are never stored, and the softmax statistics are per head.
+  bf16x8 qa[KSQ];
+  {
+    const int hq = h < p.n_heads ? h : p.n_heads - 1;
+    const uint16_t* qh = p.q + ((int64_t)t * p.n_heads + hq) * D + quad * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks)
+      qa[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + ks * 32));
+  }
+  const TokMeta meta = load_meta<MODE, HAS_B>(p, t);
+  uint32_t flags = 0;
+  const SegDesc sd = token_rows<MODE, HAS_B>(p, meta, flags);
+  if (split == 0 && blockIdx.y == 0 && tid == 0) {
+    report(p.err, flags);
+    if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
+  }
+  const int n_rows = sd.alen + sd.blen;
+  const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
+  const bool copy_rows = kGather && p.copy_out != nullptr && blockIdx.y == 0;
+  attend_tiles<D, MODE, HAS_B, 256, false, false>(p, sm, t, split, n_splits, row_begin, row_end,
+                                                  sd, pidx, nullptr, qa, nullptr, copy_rows);
+}
+
+// Select and attend in one kernel (decode step, CSA).  Every workgroup of
+// token t -- one per (row split, 16-head group) -- first runs the token's
+// exact top-k (the 1024-thread select of select_core.h, repeated by each
+// workgroup so that no kernel boundary or global handoff separates the two
+// stages), then keeps the selected block indices of its own rows in LDS and
+// runs the tile loop over them and the SWA rows.  The select's LDS is reused
+// for the tiles.  Workgroup (0, 0) of each token writes the token's idx row
+// and count.
+constexpr int kFuseThreads = sel::kThreads;
+constexpr int kFuseMaxTiles = 4;  // tiles per split the fused kernel takes
+
+template <int D>
+union FusedSmem {
+  sel::SelShared s;
+  AttSmem<D> a;
+};
+
+template <int D, bool HAS_B>
+__global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunch sl,
+                                                                     AttendLaunch p,
+                                                                     int tiles_per_split,
+                                                                     int n_splits) {
+  constexpr int KSQ = D / 32;
+  constexpr int QPR = D / 8;  // 16-byte pieces per query row
+  __shared__ FusedSmem<D> u;
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[kHeadsPerWg * (D + 8)];
+  __shared__ int32_t selrow[kFuseMaxTiles * kRT];
+  const int t = blockIdx.z;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int row_begin = split * tiles_per_split * kRT;
+
+  // The queries of the 16 heads (clamped to the last real head) and the row
+  // metadata are loaded before the select, which hides their latency.
+  u32x4 qv = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kHeadsPerWg * QPR) {
+    const int hl = tid / QPR;
+    const int hq = min((int)blockIdx.y * kHeadsPerWg + hl, p.n_heads - 1);
+    qv = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)t * p.n_heads + hq) * D +
+                                         (tid - hl * QPR) * 8);
+  }
+  TokMeta meta{};
+  meta.a_row0 = p.a_row0 != nullptr ? p.a_row0[t] : (int64_t)t * p.a_stride;
+  if constexpr (HAS_B) {
+    meta.b_row0 = p.b_row0[t];
+    meta.b_len = p.b_len[t];
+  }
+
+  const sel::SelResult r = sel::select_token(
+      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.top_k,
+      sl.cand + (int64_t)t * sl.waves_per_token * sl.cand_m,
+      sl.nvalid + (int64_t)t * sl.waves_per_token, sl.waves_per_token, sl.blocks_per_wave,
+      sl.cand_m, u.s);
+
+  if (tid < kHeadsPerWg * QPR) {
+    const int hl = tid / QPR;
+    *reinterpret_cast<u32x4*>(&qlds[hl * (D + 8) + (tid - hl * QPR) * 8]) = qv;
+  }
+  for (int i = tid; i < tiles_per_split * kRT; i += kFuseThreads) {
+    const uint32_t rr = (uint32_t)(row_begin + i);
+    selrow[i] = rr < r.emitted ? (r.listed ? u.s.outl[rr] : (int32_t)rr) : 0;
+  }
+  meta.a_cnt = (int32_t)r.emitted;
+  uint32_t flags = 0;
+  const SegDesc sd = token_rows<kModeGather, HAS_B>(p, meta, flags);
+  if (split == 0 && blockIdx.y == 0) {
+    int32_t* out = sl.idx + (int64_t)t * sl.top_k;
+    for (uint32_t i = tid; i < (uint32_t)sl.top_k; i += kFuseThreads)
+      out[i] = i < r.emitted ? (r.listed ? u.s.outl[i] : (int32_t)i) : -1;
+    if (tid == 0) {
+      sl.count[t] = (int32_t)r.emitted;
+      report(p.err, flags | r.flags);
+      if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
+    }
+  }
+  const int n_rows = sd.alen + sd.blen;
+  const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
+  const bool copy_rows = p.copy_out != nullptr && blockIdx.y == 0;
+  const bf16x8 qa_unused[KSQ] = {};
+  // attend_tiles starts with a barrier: the select's LDS is free after it
+  attend_tiles<D, kModeGather, HAS_B, kFuseThreads, true, true>(
+      p, u.a, t, split, n_splits, row_begin, row_end, sd, 0, selrow, qa_unused, qlds, copy_rows);
 }
 
 // Merge of the split partials of one (token, head).  Wave w takes splits
@@ -527,7 +652,50 @@ hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The fused kernel takes a launch whose grid fills the chip at most once
+// (one 1024-thread workgroup per CU by its LDS), so that the repeated selects
+// run side by side, and whose splits fit its LDS list of selected rows.
+bool fused_fits(const SplitPlan& sp, int T, int n_heads) {
+  const int n_hg = (n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
+  return sp.tiles_per_split <= kFuseMaxTiles && (int64_t)sp.n_splits * n_hg * T <= 256;
+}
+
+template <int D>
+hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStream_t s) {
+  const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
+  const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
+  dim3 grid((unsigned)sp.n_splits, (unsigned)n_hg, (unsigned)a.T);
+  if (a.kv_b != nullptr)
+    hipLaunchKernelGGL((select_attend_kernel<D, true>), grid, dim3(kFuseThreads), 0, s, sl, a,
+                       sp.tiles_per_split, sp.n_splits);
+  else
+    hipLaunchKernelGGL((select_attend_kernel<D, false>), grid, dim3(kFuseThreads), 0, s, sl, a,
+                       sp.tiles_per_split, sp.n_splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.n_splits == 1) return e;
+  hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),
+                     dim3(256), 0, s, a, sp.n_splits);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool select_attend_fits(int T, int n_heads, int max_rows) {
+  return T > 0 && fused_fits(plan_splits(T, n_heads, max_rows), T, n_heads);
+}
+
+hipError_t launch_select_attend(const SelectLaunch& sl, const AttendLaunch& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (!select_attend_fits(a.T, a.n_heads, a.max_rows) || a.sel_stride != sl.top_k)
+    return hipErrorInvalidValue;
+  switch (a.head_dim) {
+    case 64: return launch_fused_d<64>(sl, a, s);
+    case 128: return launch_fused_d<128>(sl, a, s);
+    case 256: return launch_fused_d<256>(sl, a, s);
+    case 512: return launch_fused_d<512>(sl, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 size_t attend_ws_bytes(int T, int n_heads, int head_dim, int max_rows) {
   const SplitPlan sp = plan_splits(T, n_heads, max_rows);

@@ -206,4 +206,17 @@ struct AttendLaunch {
 size_t attend_ws_bytes(int T, int n_heads, int head_dim, int max_rows);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 
+// Top-k and gather-mode attention in one kernel (decode step, CSA).  The
+// attention half takes its selection from the select, not from sel_idx /
+// sel_cnt; idx and count are still written.
+struct SelectLaunch {
+  const float* scores; int64_t ld; const int64_t* pos; const int32_t* n_comp;
+  int ratio, top_k;
+  const uint64_t* cand; const uint32_t* nvalid;
+  int waves_per_token, blocks_per_wave, cand_m;
+  int32_t* idx; int32_t* count;
+};
+bool select_attend_fits(int T, int n_heads, int max_rows);
+hipError_t launch_select_attend(const SelectLaunch& s, const AttendLaunch& a, hipStream_t st);
+
 }  // namespace csa
