@@ -167,7 +167,7 @@ csa_status csa_index_score(const uint16_t* q_idx, const float* w, const uint16_t
   L.q_idx = q_idx; L.w = w; L.k_idx = k_idx; L.k_rows = k_rows;
   L.pos = pos; L.seq_kv = seq_kv; L.n_comp = n_comp;
   L.T = T; L.n_ih = n_ih; L.ihd = ihd; L.ratio = ratio;
-  L.scores = scores; L.ld = ld; L.cand = nullptr; L.nvalid = nullptr; L.cand_m = 0; L.err = err;
+  L.scores = scores; L.ld = ld; L.cand = CandArgs{}; L.err = err;
   return hip_status(launch_index_score(L, static_cast<hipStream_t>(stream)));
 }
 
@@ -278,7 +278,7 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   I.pos = a->pos; I.seq_kv = a->seq_kv; I.n_comp = a->n_comp;
   I.T = a->T; I.n_ih = a->n_ih; I.ihd = a->ihd; I.ratio = a->ratio;
   I.scores = scores; I.ld = a->max_vis;
-  I.cand = tw.cand; I.nvalid = tw.nvalid; I.cand_m = tp.cand_m; I.err = a->err;
+  I.cand = cand_args(tp, tw); I.err = a->err;
   hipError_t e = launch_index_score(I, st);
   if (e != hipSuccess) return hip_status(e);
   L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
@@ -292,8 +292,8 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
     SelectLaunch S{};
     S.scores = scores; S.ld = a->max_vis; S.pos = a->pos; S.n_comp = a->n_comp;
     S.ratio = a->ratio; S.top_k = a->top_k;
-    S.cand = tw.cand; S.nvalid = tw.nvalid; S.waves_per_token = tp.waves_per_token;
-    S.blocks_per_wave = tp.blocks_per_wave; S.cand_m = tp.cand_m;
+    S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
+    S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
     S.idx = idx; S.count = count;
     e = launch_select_attend(S, L, st);
   } else {

@@ -478,9 +478,9 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
 
   const sel::SelResult r = sel::select_token(
       sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.top_k,
-      sl.cand + (int64_t)t * sl.waves_per_token * sl.cand_m,
-      sl.nvalid + (int64_t)t * sl.waves_per_token, sl.waves_per_token, sl.blocks_per_wave,
-      sl.cand_m, u.s);
+      sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
+      sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
+      sl.blocks_per_group, u.s);
 
   if (tid < kHeadsPerWg * QPR) {
     const int hl = tid / QPR;

@@ -51,12 +51,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // ascend in (q, lane) order.  Writes the m largest composite keys (larger
 // score, then lower index) to out[0..m) in descending order, so out[m-1] is
 // the smallest key of the list; with fewer than m valid blocks the list is
-// zero-padded.  Returns the number of valid blocks.  One key per round: the
-// wave maximum of the 32-bit score keys, then the lowest (q, lane) holding it.
+// zero-padded.  Returns the number of valid blocks and, in *last (every
+// lane), the smallest listed key (0 if none).  One key per round: the wave
+// maximum of the 32-bit score keys, then the lowest (q, lane) holding it.
 template <int KPL>
 __device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const bool (&ok)[KPL],
                                                const uint32_t (&blk)[KPL], uint32_t m,
-                                               uint64_t* out) {
+                                               uint64_t* out, uint64_t* last) {
   const int lane = threadIdx.x & 63;
   uint32_t sk[KPL];  // 0 = empty (score keys of non-NaN scores are nonzero)
   uint32_t n_ok = 0;
@@ -66,6 +67,7 @@ __device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const boo
     n_ok += (uint32_t)__popcll(__ballot(ok[q]));
   }
   const uint32_t take = n_ok < m ? n_ok : m;
+  uint64_t key_r = 0ull;
   for (uint32_t r = 0; r < take; ++r) {
     uint32_t lm = 0;
 #pragma unroll
@@ -83,18 +85,22 @@ __device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const boo
         }
       }
     }
-    if (lane == __ffsll((unsigned long long)mask) - 1) {
-      uint32_t ob = 0;
+    const int owner = __ffsll((unsigned long long)mask) - 1;
+    uint32_t ob = 0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+      if (q == oq) ob = blk[q];
+    ob = (uint32_t)__builtin_amdgcn_readlane((int)ob, owner);
+    key_r = ((uint64_t)M << 32) | (uint32_t)~ob;
+    if (lane == owner) {
 #pragma unroll
       for (int q = 0; q < KPL; ++q)
-        if (q == oq) {
-          ob = blk[q];
-          sk[q] = 0u;
-        }
-      out[r] = ((uint64_t)M << 32) | (uint32_t)~ob;
+        if (q == oq) sk[q] = 0u;
+      out[r] = key_r;
     }
   }
   for (uint32_t i = take + (uint32_t)lane; i < m; i += 64) out[i] = 0ull;
+  *last = key_r;
   return n_ok;
 }
 
@@ -131,6 +137,82 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Candidate lists of the top-k, written by the indexer epilogue (or by
+// score_cands_kernel for caller-given scores) and read by the select.  A
+// token's blocks are cut into groups of consecutive blocks: one indexer
+// wave's blocks, or with merging one indexer workgroup's.  Group g of token t
+// has list_len composite keys at cand[(t*groups_per_token + g)*list_len],
+// descending and zero-padded, and a bound gcut[t*groups_per_token + g] that
+// is >= the key of every block of the group missing from the list (0: the
+// list holds every block of the group).
+constexpr int kIndexWaves = 8;      // waves per indexer workgroup
+constexpr int kMergeMaxWaveM = 8;   // merged waves' lists fit one wave: kIndexWaves * 8 = 64
+struct CandArgs {
+  uint64_t* cand; uint64_t* gcut;
+  int wave_m;            // keys each wave keeps of its own blocks
+  int merge;             // 1: a group is a workgroup; its waves' lists are merged
+  int list_len;          // keys per group list
+  int groups_per_token;
+};
+
+// Candidate-list epilogue.  Lane L of the calling wave holds score ks[q] of
+// block blk[q] where ok[q] (indices ascending in (q, lane) order).  Without
+// merging the wave's top-wave_m keys are its group's list and the group bound
+// is the list's last key when the wave has more valid blocks.  With merging
+// every wave of the workgroup calls this (it holds a barrier): each wave's
+// top-wave_m and bound go to LDS (wave w's kMergeMaxWaveM + 1 words at
+// lds + w*lds_stride), and wave 0 keeps the list_len largest of those
+// kIndexWaves*wave_m keys.  A block missing from the merged list is either
+// below the largest key left out of it, or missing from its wave's list and
+// so below that wave's last key; the bound is the larger of those.
+template <int KPL>
+__device__ __forceinline__ void cand_epilogue(const float (&ks)[KPL], const bool (&ok)[KPL],
+                                              const uint32_t (&blk)[KPL], const CandArgs& ca,
+                                              int64_t t, int64_t wave_in_token,
+                                              int64_t wg_in_token, uint64_t* lds,
+                                              int lds_stride) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t last;
+  if (!ca.merge) {
+    const int64_t g = t * ca.groups_per_token + wave_in_token;
+    const uint32_t n_ok =
+        wave_top_m<KPL>(ks, ok, blk, (uint32_t)ca.wave_m, ca.cand + g * ca.list_len, &last);
+    if (lane == 0) ca.gcut[g] = n_ok > (uint32_t)ca.wave_m ? last : 0ull;
+    return;
+  }
+  uint64_t* mine = lds + wave * lds_stride;
+  const uint32_t n_ok = wave_top_m<KPL>(ks, ok, blk, (uint32_t)ca.wave_m, mine, &last);
+  if (lane == 0) mine[kMergeMaxWaveM] = n_ok > (uint32_t)ca.wave_m ? last : 0ull;
+  __syncthreads();
+  if (wave != 0) return;
+  const int m = ca.wave_m;
+  const int w = lane / m;
+  const uint64_t key = lane < kIndexWaves * m ? lds[w * lds_stride + (lane - w * m)] : 0ull;
+  // rank among the 64 lanes' keys; equal keys (only zeros) rank by lane
+  const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
+  uint32_t rank = 0;
+  for (int j = 0; j < 64; ++j) {
+    const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
+    rank += (kj > key || (kj == key && j < lane)) ? 1u : 0u;
+  }
+  const int64_t g = t * ca.groups_per_token + wg_in_token;
+  if (rank < (uint32_t)ca.list_len) ca.cand[g * ca.list_len + rank] = key;
+  const uint64_t out_mask = __ballot(rank == (uint32_t)ca.list_len);
+  uint64_t cut = 0ull;
+  if (out_mask != 0ull) {
+    const int o = __ffsll((unsigned long long)out_mask) - 1;
+    cut = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, o) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)klo, o);
+  }
+#pragma unroll
+  for (int v = 0; v < kIndexWaves; ++v) {
+    const uint64_t wc = lds[v * lds_stride + kMergeMaxWaveM];
+    cut = wc > cut ? wc : cut;
+  }
+  if (lane == 0) ca.gcut[g] = cut;
+}
+
 // ---------------------------------------------------------------------------
 // Internal launchers (host).  Arguments are validated by the C ABI layer.
 // ---------------------------------------------------------------------------
@@ -139,12 +221,9 @@ struct IndexScoreLaunch {
   const int64_t* pos; const int64_t* seq_kv; const int32_t* n_comp;
   int T, n_ih, ihd, ratio;
   float* scores; int64_t ld;
-  uint64_t* cand;   // [T, waves_per_token, cand_m] or nullptr: per-wave top-m keys
-  uint32_t* nvalid; // [T, waves_per_token] valid blocks of each wave
-  int cand_m;
+  CandArgs cand;    // cand.cand == nullptr: no candidate lists
   uint32_t* err;
 };
-constexpr int kIndexWaves = 8;  // waves per indexer workgroup
 struct IndexPlan {
   int tiles_per_wave, wgs_per_token;
   int waves_per_token() const { return wgs_per_token * kIndexWaves; }
@@ -153,20 +232,23 @@ struct IndexPlan {
 IndexPlan plan_index(int T, int64_t ld);
 hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s);
 
-// Top-k (see topk.hip).  Candidate layout shared with the indexer epilogue.
-constexpr int kPoolCap = 12288;  // keys the select workgroup holds in LDS
+// Top-k (see topk.hip).
+constexpr int kPoolCap = 12288;   // keys the select workgroup holds in registers
+constexpr int kMaxGroups = 2048;  // group bounds the select holds (two per thread)
 struct TopkPlan {
-  int waves_per_token;   // candidate lists per token
-  int blocks_per_wave;   // blocks behind each list
-  int cand_m;            // keys per list (0: every token selects from its scores directly)
+  int waves_per_token, blocks_per_wave;  // indexer geometry
+  int wave_m, merge;                     // see CandArgs
+  int list_len;                          // keys per group list (0: no lists)
+  int groups_per_token, blocks_per_group;
 };
 TopkPlan plan_topk(int T, int64_t ld, int top_k);
 struct TopkWs {
-  uint64_t* cand;    // [T, waves_per_token, cand_m]
-  uint32_t* nvalid;  // [T, waves_per_token]
+  uint64_t* cand;  // [T, groups_per_token, list_len]
+  uint64_t* gcut;  // [T, groups_per_token]
   size_t bytes;
 };
 TopkWs topk_ws_layout(void* ws, int T, const TopkPlan& p);
+CandArgs cand_args(const TopkPlan& p, const TopkWs& w);
 hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* pos,
                               const int32_t* n_comp, int T, int ratio, const TopkPlan& p,
                               const TopkWs& ws, uint32_t* err, hipStream_t s);
@@ -212,8 +294,8 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 struct SelectLaunch {
   const float* scores; int64_t ld; const int64_t* pos; const int32_t* n_comp;
   int ratio, top_k;
-  const uint64_t* cand; const uint32_t* nvalid;
-  int waves_per_token, blocks_per_wave, cand_m;
+  const uint64_t* cand; const uint64_t* gcut;
+  int list_len, groups_per_token, blocks_per_group;
   int32_t* idx; int32_t* count;
 };
 bool select_attend_fits(int T, int n_heads, int max_rows);

@@ -32,8 +32,9 @@
 //     waited for with explicit vmcnt counts; the tile loop is unrolled so the
 //     per-tile scores stay in VGPRs until the wave's tiles are done.
 //
-// Optionally the epilogue also emits each wave's top-m composite selection
-// keys (score, then lower block index) -- the candidate lists of the top-k.
+// Optionally the epilogue also emits the candidate lists of the top-k: each
+// wave's top-m composite selection keys (score, then lower block index),
+// merged per workgroup when the plan asks for it.
 #include "csa_common.h"
 
 namespace csa {
@@ -62,8 +63,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     const uint16_t* __restrict__ k_idx, int64_t k_rows,
     const int64_t* __restrict__ pos, const int64_t* __restrict__ seq_kv,
     const int32_t* __restrict__ n_comp, int n_ih, int ratio,
-    float* __restrict__ scores, int64_t ld, uint64_t* __restrict__ cand,
-    uint32_t* __restrict__ nvalid, int cand_m, uint32_t* __restrict__ err,
+    float* __restrict__ scores, int64_t ld, CandArgs ca, uint32_t* __restrict__ err,
     int tiles_per_wave) {
   constexpr int KS = IHD / 16;          // MFMA k-steps (one 16-byte chunk per lane each)
   constexpr int CPR = IHD / 8;          // 16-byte chunks per key or query row
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   const int64_t n_tiles = (n_vis + kTileN - 1) / kTileN;
   const int64_t tile_begin = ((int64_t)blockIdx.x * kWaves + wave) * tiles_per_wave;
   const int64_t tile_end = min(tile_begin + (int64_t)tiles_per_wave, n_tiles);
-  const int64_t wslot = (int64_t)t * gridDim.x * kWaves + (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t wave_in_token = (int64_t)blockIdx.x * kWaves + wave;
   const bool active = tile_begin < tile_end;  // wave-uniform
   const char* kbase = reinterpret_cast<const char*>(k_idx + row0 * IHD);
 
@@ -173,10 +173,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     if (tile_begin + 1 < tile_end) issue_tile(tile_begin + 1, 1);
   }
   __syncthreads();  // the query block is in LDS for every wave
+  // After its last tile each wave's own tile buffers hold its candidate list
+  // for the workgroup merge (no DMA into them is pending by then).
+  uint64_t* cand_lds = reinterpret_cast<uint64_t*>(&ktile[0][0][0]);
+  constexpr int kCandStride = 2 * TILE_CHUNKS * 2;  // u64 words per wave's buffers
+  constexpr int KPL = kMaxTpw / 2;
   if (!active) {
-    if (cand != nullptr && lane == 0) {
-      nvalid[wslot] = 0u;
-      for (int i = 0; i < cand_m; ++i) cand[wslot * cand_m + i] = 0ull;
+    if (ca.cand != nullptr) {  // empty list and bound (and the merge barrier)
+      float ks[KPL] = {};
+      bool ok[KPL] = {};
+      uint32_t blk[KPL] = {};
+      cand_epilogue<KPL>(ks, ok, blk, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
     }
     return;
   }
@@ -239,9 +246,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     if (q < nt && half == 0 && blk < n_vis) srow[blk] = sc[q];
   }
 
-  if (cand != nullptr) {
+  if (ca.cand != nullptr) {
     // both half-waves hold every tile's scores: half h takes tiles 2p + h
-    constexpr int KPL = kMaxTpw / 2;
     float ks[KPL];
     bool ok[KPL];
     uint32_t blk[KPL];
@@ -255,8 +261,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       ok[p] = q < nt && b < n_vis;
       blk[p] = (uint32_t)b;
     }
-    const uint32_t n_ok = wave_top_m<KPL>(ks, ok, blk, (uint32_t)cand_m, cand + wslot * cand_m);
-    if (lane == 0) nvalid[wslot] = n_ok;
+    cand_epilogue<KPL>(ks, ok, blk, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
   }
 }
 
@@ -265,7 +270,7 @@ hipError_t launch_t(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t s
   dim3 grid(p.wgs_per_token, a.T);
   hipLaunchKernelGGL((index_score_kernel<IHD, MT>), grid, dim3(kWaves * 64), 0, s, a.q_idx, a.w,
                      a.k_idx, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.n_ih, a.ratio, a.scores,
-                     a.ld, a.cand, a.nvalid, a.cand_m, a.err, p.tiles_per_wave);
+                     a.ld, a.cand, a.err, p.tiles_per_wave);
   return hipGetLastError();
 }
 

@@ -10,15 +10,13 @@
 // The workgroup selects from a key set held in registers (12 keys per
 // thread) plus an LDS overflow area:
 //   * n_vis <= kPoolCap: the keys are every visible block (exact, direct);
-//   * otherwise the keys are the candidate lists -- the top-m keys of every
-//     group of blocks handled by one indexer wave, written by the indexer
-//     epilogue (or score_cands_kernel).  Let T1 be the k_eff-th largest
-//     listed key.  A group whose list is full (it has more than m blocks) and
-//     whose m-th key is >= T1 may hold unlisted blocks above T1; its unlisted
-//     blocks are added and the threshold is found again.  Every other
-//     unlisted block is below its group's m-th key < T1, below k_eff listed
-//     keys, so the result is exact.  At most k_eff/m groups can qualify (each
-//     puts m keys >= T1 into the set, and only k_eff keys are >= T1);
+//   * otherwise the keys are the candidate lists of the groups that cover
+//     the row (see CandArgs).  Let T1 be the k_eff-th largest listed key.  A
+//     group whose bound (>= every key it did not list) is >= T1 may hold
+//     unlisted blocks at or above T1: its listed keys leave the set and all
+//     its visible blocks join it, and the threshold is found again.  Every
+//     other unlisted block is below T1, below k_eff listed keys, so the
+//     result is exact;
 //   * if the extra blocks would not fit, or a long row has no lists, the
 //     select runs over the token's scores in global memory (slow, exact).
 //
@@ -61,9 +59,8 @@ struct SelShared {
   uint64_t xk[kXCap];
   uint64_t list[kListCap];
   uint32_t hist[kBins];
-  uint32_t ov_w[kMaxOv];
-  uint32_t ov_nv[kMaxOv];
-  uint64_t ov_cut[kMaxOv];
+  uint32_t ov_g[kMaxOv];                  // flagged groups (re-scanned whole)
+  uint32_t gflag[kMaxGroups / 32];        // the same groups as a bitmap
   int32_t outl[kMaxTopK];                 // the selection, ascending, before the output copy
   uint32_t scratch[2 * kWaves + 8];
   uint32_t rc[kWaves];                    // per-wave count / score-word range of kth_key
@@ -427,59 +424,43 @@ struct SelResult {
 
 // Top-k of one token over its scores row `srow` (ld entries, n_vis of them
 // visible): every thread of the 1024-thread workgroup calls this with the same
-// arguments.  `cand`/`nval` are the token's candidate lists (cand_m keys per
-// group, zero keys for empty slots) and group sizes; cand_m == 0 means none.
-// On return (after a barrier) the selection is described by the result and,
-// when listed, by sh.outl in ascending block order.
+// arguments.  `cand`/`gcut` are the token's candidate lists and group bounds
+// (list_len keys per group of blocks_per_group blocks, groups_per_token
+// groups; list_len == 0 means none).  On return (after a barrier) the
+// selection is described by the result and, when listed, by sh.outl in
+// ascending block order.
 __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow, int64_t ld,
                                                   int64_t pos_t, int32_t ncomp_t, int ratio,
                                                   int top_k, const uint64_t* __restrict__ cand,
-                                                  const uint32_t* __restrict__ nval,
-                                                  int waves_per_token, int blocks_per_wave,
-                                                  int cand_m, SelShared& sh) {
+                                                  const uint64_t* __restrict__ gcut, int list_len,
+                                                  int groups_per_token, int blocks_per_group,
+                                                  SelShared& sh) {
   const int tid = threadIdx.x;
   // The candidate lists do not depend on the row length, so they are loaded
-  // before it is known: every list of the token (the indexer writes all of
-  // them, zero keys for waves without blocks) with the size of the group
-  // whose m-th key each slot holds.
-  const uint32_t m = cand_m > 0 ? (uint32_t)cand_m : 1u;
-  const uint32_t CT = cand_m > 0 ? min((uint32_t)waves_per_token * m, (uint32_t)kPoolCap) : 0u;
+  // before it is known: every list of the token (empty groups have zero keys)
+  // and the bounds of up to two groups per thread.  Every load is
+  // unconditional (indices clamped into the arrays) and masked afterwards,
+  // so that all of them are in flight together.
+  const uint32_t L = list_len > 0 ? (uint32_t)list_len : 1u;
+  const uint32_t NG = list_len > 0 ? (uint32_t)groups_per_token : 0u;
+  const uint32_t CT = NG * L;  // <= kPoolCap, and NG <= kMaxGroups (plan_topk)
   uint64_t key[KPT];
-  uint32_t nv[KPT];
+  uint64_t gc[2];
   if (CT > 0u) {
-    // slot j = tid + i*kThreads is key j % m of group j / m; both are carried
-    // from slot to slot instead of divided out per slot.  Every load is
-    // unconditional (indices clamped into the lists) and masked afterwards,
-    // so that all of them are in flight together.
-    const uint32_t dq = (uint32_t)kThreads / m, dr = (uint32_t)kThreads - dq * m;
-    const uint32_t last_g = (CT - 1u) / m;
-    uint32_t q = (uint32_t)tid / m, r = (uint32_t)tid - q * m;
-    bool cut_slot[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-      key[i] = cand[min(j, CT - 1u)];
-      nv[i] = nval[min(q, last_g)];
-      cut_slot[i] = j < CT && r == m - 1u;
-      q += dq;
-      r += dr;
-      if (r >= m) {
-        r -= m;
-        ++q;
-      }
-    }
+    for (int i = 0; i < KPT; ++i) key[i] = cand[min((uint32_t)tid + (uint32_t)i * kThreads, CT - 1u)];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-      if (j >= CT) key[i] = 0ull;
-      if (!cut_slot[i]) nv[i] = 0u;
-    }
+    for (int i = 0; i < 2; ++i) gc[i] = gcut[min((uint32_t)tid + (uint32_t)i * kThreads, NG - 1u)];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if ((uint32_t)tid + (uint32_t)i * kThreads >= CT) key[i] = 0ull;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if ((uint32_t)tid + (uint32_t)i * kThreads >= NG) gc[i] = 0ull;
   } else {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      key[i] = 0ull;
-      nv[i] = 0u;
-    }
+    for (int i = 0; i < KPT; ++i) key[i] = 0ull;
+    gc[0] = gc[1] = 0ull;
   }
   // the emission bitmap is cleared while those loads are in flight
   {
@@ -490,6 +471,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
     sh.n_ov = 0u;
     sh.n_x = 0u;
   }
+  if (tid < kMaxGroups / 32) sh.gflag[tid] = 0u;
   uint32_t f = 0;
   int64_t n_vis = visible_count(pos_t, ratio, ncomp_t, &f);
   if (n_vis > ld) {
@@ -508,9 +490,8 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
     res.listed = true;
     uint32_t n_x = 0;
     uint32_t nk = 0;  // register key slots in use (i*kThreads < nk)
-    // lists of every group of a long row are needed (plan_topk sets
-    // cand_m = 0 when they would not fit the key set)
-    bool global_path = n_vis > kPoolCap && (cand_m == 0 || (uint32_t)waves_per_token * m > (uint32_t)kPoolCap);
+    // a long row without candidate lists selects over its scores in memory
+    bool global_path = n_vis > kPoolCap && CT == 0u;
     uint64_t thr = 0ull;
     if (n_vis <= kPoolCap) {
       // ---- direct: every visible block is a key ----
@@ -522,35 +503,27 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
       for (int i = 0; i < KPT; ++i) {
         const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
         key[i] = j < n ? block_key(sv[i], j) : 0ull;
-        nv[i] = 0u;
       }
       nk = n;
       thr = kth_key(key, nk, 0, k_eff, sh);
     } else if (!global_path) {
-      // ---- candidate lists of the nw groups that cover the row ----
-      const int G = blocks_per_wave;
-      const uint32_t nw = (uint32_t)((n_vis + G - 1) / G);
-      const uint32_t C = min(nw * m, CT);
+      // ---- candidate lists of the ng groups that cover the row ----
+      const uint32_t G = (uint32_t)blocks_per_group;
+      const uint32_t ng = (uint32_t)((n_vis + G - 1) / G);
+      const uint32_t C = min(ng * L, CT);
       nk = C;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
-        if (j >= C) {
-          key[i] = 0ull;
-          nv[i] = 0u;
-        }
-      }
+      for (int i = 0; i < KPT; ++i)
+        if ((uint32_t)tid + (uint32_t)i * kThreads >= C) key[i] = 0ull;
       const uint64_t t1 = C >= k_eff ? kth_key(key, nk, 0, k_eff, sh) : 0ull;
       // groups that may hold unlisted blocks at or above T1
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        if ((uint32_t)i * kThreads < nk && nv[i] > m && (t1 == 0ull || key[i] >= t1)) {
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t g = (uint32_t)tid + (uint32_t)i * kThreads;
+        if (g < ng && gc[i] != 0ull && (t1 == 0ull || gc[i] >= t1)) {
           const uint32_t slot = atomicAdd(&sh.n_ov, 1u);
-          if (slot < (uint32_t)kMaxOv) {
-            sh.ov_w[slot] = ((uint32_t)tid + (uint32_t)i * kThreads) / m;
-            sh.ov_nv[slot] = nv[i];
-            sh.ov_cut[slot] = key[i];
-          }
+          if (slot < (uint32_t)kMaxOv) sh.ov_g[slot] = g;
+          atomicOr(&sh.gflag[g >> 5], 1u << (g & 31));
         }
       }
       __syncthreads();
@@ -558,15 +531,32 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
       global_path = n_ov > (uint32_t)kMaxOv || t1 == 0ull;
       thr = t1;
       if (!global_path && n_ov > 0) {
-        const uint32_t unlisted =
-            block_sum((uint32_t)tid < n_ov ? sh.ov_nv[tid] - m : 0u, sh.scratch);
-        if (unlisted > (uint32_t)kXCap) {
+        uint32_t span_g = 0;  // visible blocks of flagged group tid
+        if ((uint32_t)tid < n_ov) {
+          const int64_t b0 = (int64_t)sh.ov_g[tid] * G;
+          span_g = (uint32_t)min((int64_t)G, n_vis - b0);
+        }
+        const uint32_t extra = block_sum(span_g, sh.scratch);
+        if (extra > (uint32_t)kXCap) {
           global_path = true;
         } else {
-          // every block of the flagged groups that is below the group's m-th
-          // key (i.e. not listed) joins the key set
+          // a flagged group's listed keys leave the register set ...
+          const uint32_t dq = (uint32_t)kThreads / L, dr = (uint32_t)kThreads - dq * L;
+          uint32_t q = (uint32_t)tid / L, r = (uint32_t)tid - q * L;
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) {
+            if ((uint32_t)i * kThreads < nk && q < ng && ((sh.gflag[q >> 5] >> (q & 31)) & 1u))
+              key[i] = 0ull;
+            q += dq;
+            r += dr;
+            if (r >= L) {
+              r -= L;
+              ++q;
+            }
+          }
+          // ... and every visible block of the group joins the LDS extras
           constexpr int XB = 4;
-          const uint32_t span = n_ov * (uint32_t)G;
+          const uint32_t span = n_ov * G;
           for (uint32_t e0 = 0; e0 < span; e0 += XB * kThreads) {
             uint32_t blk[XB];
             bool ok[XB];
@@ -574,19 +564,16 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
 #pragma unroll
             for (int u = 0; u < XB; ++u) {
               const uint32_t e = e0 + (uint32_t)u * kThreads + tid;
-              const uint32_t g = e / (uint32_t)G, off = e - g * (uint32_t)G;
-              ok[u] = e < span && off < sh.ov_nv[g < n_ov ? g : 0];
-              blk[u] = ok[u] ? sh.ov_w[g] * (uint32_t)G + off : 0u;
+              const uint32_t g = e / G;
+              const int64_t b = (int64_t)sh.ov_g[g < n_ov ? g : 0] * G + (e - g * G);
+              ok[u] = e < span && b < n_vis;
+              blk[u] = ok[u] ? (uint32_t)b : 0u;
             }
 #pragma unroll
             for (int u = 0; u < XB; ++u) fv[u] = ok[u] ? srow[blk[u]] : 0.0f;
 #pragma unroll
-            for (int u = 0; u < XB; ++u) {
-              const uint32_t e = e0 + (uint32_t)u * kThreads + tid;
-              const uint64_t c = ok[u] ? block_key(fv[u], blk[u]) : 0ull;
-              const bool add = ok[u] && c < sh.ov_cut[e / (uint32_t)G];
-              wave_append(add, c, sh.xk, &sh.n_x, kXCap);
-            }
+            for (int u = 0; u < XB; ++u)
+              wave_append(ok[u], ok[u] ? block_key(fv[u], blk[u]) : 0ull, sh.xk, &sh.n_x, kXCap);
           }
           __syncthreads();
           n_x = min(sh.n_x, (uint32_t)kXCap);

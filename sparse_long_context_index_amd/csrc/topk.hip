@@ -14,16 +14,16 @@ namespace {
 __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ n_comp, int ratio, int top_k,
-    const uint64_t* __restrict__ cand_all, const uint32_t* __restrict__ nvalid_all,
-    int waves_per_token, int blocks_per_wave, int cand_m, int32_t* __restrict__ idx,
+    const uint64_t* __restrict__ cand_all, const uint64_t* __restrict__ gcut_all, int list_len,
+    int groups_per_token, int blocks_per_group, int32_t* __restrict__ idx,
     int32_t* __restrict__ count, uint32_t* __restrict__ err) {
   __shared__ sel::SelShared sh;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   const sel::SelResult r = sel::select_token(
       scores + (int64_t)t * ld, ld, pos[t], n_comp[t], ratio, top_k,
-      cand_all + (int64_t)t * waves_per_token * cand_m, nvalid_all + (int64_t)t * waves_per_token,
-      waves_per_token, blocks_per_wave, cand_m, sh);
+      cand_all + (int64_t)t * groups_per_token * list_len, gcut_all + (int64_t)t * groups_per_token,
+      list_len, groups_per_token, blocks_per_group, sh);
   // one coalesced pass writes the selection and the -1 padding
   int32_t* out = idx + (int64_t)t * top_k;
   for (uint32_t i = tid; i < (uint32_t)top_k; i += sel::kThreads)
@@ -34,13 +34,18 @@ __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
   }
 }
 
-// Candidate lists from caller-given scores (same layout as the indexer's).
-constexpr int kCandThreads = 256;
+// Candidate lists from caller-given scores, in the indexer's layout: a
+// workgroup of kIndexWaves waves per indexer workgroup, wave w scoring the
+// same blocks as the indexer wave it stands for.
+constexpr int kCandThreads = kIndexWaves * 64;
 __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
-    const int32_t* __restrict__ n_comp, int ratio, int blocks_per_wave, int cand_m,
-    uint64_t* __restrict__ cand, uint32_t* __restrict__ nvalid, uint32_t* __restrict__ err) {
-  constexpr int KPL = 8;  // up to 8 x 32 = 256 blocks per group
+    const int32_t* __restrict__ n_comp, int ratio, int blocks_per_wave, CandArgs ca,
+    uint32_t* __restrict__ err) {
+  constexpr int KPL = 8;  // up to 8 x 32 = 256 blocks per wave
+  constexpr int KPH = KPL / 2;
+  constexpr int kStride = kMergeMaxWaveM + 1;
+  __shared__ uint64_t lds[kIndexWaves * kStride];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t flags = 0;
@@ -50,13 +55,11 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
     n_vis = ld;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) report(err, flags);
-  const int64_t wg = (int64_t)blockIdx.x * (kCandThreads / 64) + wave;
-  const int64_t wslot = (int64_t)t * gridDim.x * (kCandThreads / 64) + wg;
-  const int64_t b0 = wg * blocks_per_wave;
+  const int64_t wave_in_token = (int64_t)blockIdx.x * kIndexWaves + wave;
+  const int64_t b0 = wave_in_token * blocks_per_wave;
   const int64_t b1 = min(b0 + (int64_t)blocks_per_wave, n_vis);
   const float* srow = scores + (int64_t)t * ld;
-  // half-wave h takes the 32-block pieces 2p + h of the group
-  constexpr int KPH = KPL / 2;
+  // half-wave h takes the 32-block pieces 2p + h of the wave's blocks
   float sc[KPH];
   bool ok[KPH];
   uint32_t blk[KPH];
@@ -68,41 +71,62 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
     blk[p] = (uint32_t)b;
     sc[p] = ok[p] ? srow[b] : 0.0f;
   }
-  const uint32_t n_ok = wave_top_m<KPH>(sc, ok, blk, (uint32_t)cand_m, cand + wslot * cand_m);
-  if (lane == 0) nvalid[wslot] = n_ok;
+  cand_epilogue<KPH>(sc, ok, blk, ca, t, wave_in_token, blockIdx.x, lds, kStride);
 }
 
 }  // namespace
 
 TopkPlan plan_topk(int T, int64_t ld, int top_k) {
-  (void)top_k;
   const IndexPlan ip = plan_index(T, ld);
-  TopkPlan p;
+  TopkPlan p{};
   p.waves_per_token = ip.waves_per_token();
   p.blocks_per_wave = ip.blocks_per_wave();
-  // short rows select over all their blocks; rows whose lists would not fit
-  // the select's key set (over kPoolCap groups) take its global path
-  if (ld <= kPoolCap || p.waves_per_token > kPoolCap) {
-    p.cand_m = 0;
-    return p;
-  }
-  // the lists of one token fill at most the select workgroup's registers
+  // Short rows select over all their blocks.  Rows with more groups than the
+  // select holds bounds for take its global path.
+  if (ld <= kPoolCap || p.waves_per_token > kMaxGroups) return p;
+  // every wave keeps its share of the select's key set
   int m = kPoolCap / p.waves_per_token;
   if (m > 32) m = 32;
   if (m < 1) m = 1;
-  p.cand_m = m;
+  p.wave_m = m;
+  // A workgroup merges its waves' lists into one of 16 keys when they fit one
+  // wave and the token's merged lists still hold at least three times top_k
+  // keys.  The select then holds a third as many keys, and a group's expected
+  // share of a full row's top-k is at most 16/3 keys, well inside its list.
+  constexpr int kMergedLen = 16;
+  if (kIndexWaves * m <= 64 && (int64_t)ip.wgs_per_token * kMergedLen >= 3 * (int64_t)top_k) {
+    p.merge = 1;
+    p.list_len = kMergedLen;
+    p.groups_per_token = ip.wgs_per_token;
+    p.blocks_per_group = kIndexWaves * p.blocks_per_wave;
+  } else {
+    p.list_len = m;
+    p.groups_per_token = p.waves_per_token;
+    p.blocks_per_group = p.blocks_per_wave;
+  }
   return p;
+}
+
+CandArgs cand_args(const TopkPlan& p, const TopkWs& w) {
+  CandArgs c{};
+  c.cand = w.cand;
+  c.gcut = w.gcut;
+  c.wave_m = p.wave_m;
+  c.merge = p.merge;
+  c.list_len = p.list_len;
+  c.groups_per_token = p.groups_per_token;
+  return c;
 }
 
 TopkWs topk_ws_layout(void* ws, int T, const TopkPlan& p) {
   TopkWs w{};
-  const size_t n = (size_t)T * p.waves_per_token;
-  const size_t cand_b = (n * p.cand_m * 8 + 255) & ~(size_t)255;
-  const size_t nv_b = (n * 4 + 255) & ~(size_t)255;
-  w.bytes = p.cand_m ? cand_b + nv_b : 0;
-  if (ws != nullptr && p.cand_m) {
+  const size_t n = (size_t)T * p.groups_per_token;
+  const size_t cand_b = (n * p.list_len * 8 + 255) & ~(size_t)255;
+  const size_t cut_b = (n * 8 + 255) & ~(size_t)255;
+  w.bytes = p.list_len ? cand_b + cut_b : 0;
+  if (ws != nullptr && p.list_len) {
     w.cand = static_cast<uint64_t*>(ws);
-    w.nvalid = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + cand_b);
+    w.gcut = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + cand_b);
   }
   return w;
 }
@@ -110,10 +134,10 @@ TopkWs topk_ws_layout(void* ws, int T, const TopkPlan& p) {
 hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* pos,
                               const int32_t* n_comp, int T, int ratio, const TopkPlan& p,
                               const TopkWs& ws, uint32_t* err, hipStream_t s) {
-  if (T == 0 || p.cand_m == 0) return hipSuccess;
-  dim3 grid((unsigned)(p.waves_per_token / (kCandThreads / 64)), (unsigned)T);
+  if (T == 0 || p.list_len == 0) return hipSuccess;
+  dim3 grid((unsigned)(p.waves_per_token / kIndexWaves), (unsigned)T);
   hipLaunchKernelGGL(score_cands_kernel, grid, dim3(kCandThreads), 0, s, scores, ld, pos, n_comp,
-                     ratio, p.blocks_per_wave, p.cand_m, ws.cand, ws.nvalid, err);
+                     ratio, p.blocks_per_wave, cand_args(p, ws), err);
   return hipGetLastError();
 }
 
@@ -123,8 +147,8 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int64_t* po
                               int32_t* count, uint32_t* err, hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)T), dim3(sel::kThreads), 0, s, scores, ld,
-                     pos, n_comp, ratio, top_k, ws.cand, ws.nvalid, p.waves_per_token,
-                     p.blocks_per_wave, p.cand_m, idx, count, err);
+                     pos, n_comp, ratio, top_k, ws.cand, ws.gcut, p.list_len,
+                     p.groups_per_token, p.blocks_per_group, idx, count, err);
   return hipGetLastError();
 }
 
