@@ -46,18 +46,42 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+}
+
+// Lane i of each 16-lane row receives lane i-1's value; lane 0 of a row
+// receives all ones.
+__device__ __forceinline__ uint64_t row_shr1_u64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(v >> 32), 0x111, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)v, 0x111, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One round of a wave-level selection: the largest nonzero score key over the
+// lanes (sk), its owner (the lowest lane holding it; lane order is block
+// order for equal scores), and that lane's low word.  The owner's sk is
+// cleared.  Returns the composite key.
+__device__ __forceinline__ uint64_t wave_take_max(uint32_t& sk, uint32_t lo) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t M = wave_max_u32(sk);
+  const int owner = __ffsll((unsigned long long)__ballot(sk == M)) - 1;
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_readlane((int)lo, owner);
+  if (lane == owner) sk = 0u;
+  return ((uint64_t)M << 32) | olo;
+}
+
 // Wave-level top-m of the blocks whose scores the lanes hold: for q < KPL,
 // lane L holds score sc[q] of block blk[q] where ok[q].  Block indices must
-// ascend in (q, lane) order.  Writes the m largest composite keys (larger
-// score, then lower index) to out[0..m) in descending order, so out[m-1] is
-// the smallest key of the list; with fewer than m valid blocks the list is
-// zero-padded.  Returns the number of valid blocks and, in *last (every
-// lane), the smallest listed key (0 if none).  One key per round: the wave
-// maximum of the 32-bit score keys, then the lowest (q, lane) holding it.
+// ascend in (q, lane) order.  Returns the number of valid blocks; lane r < m
+// receives in *val the r-th largest composite key (larger score, then lower
+// index), zero beyond the valid blocks.  One key per round: the wave maximum
+// of the 32-bit score keys, then the lowest (q, lane) holding it.
 template <int KPL>
 __device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const bool (&ok)[KPL],
                                                const uint32_t (&blk)[KPL], uint32_t m,
-                                               uint64_t* out, uint64_t* last) {
+                                               uint64_t* val) {
   const int lane = threadIdx.x & 63;
   uint32_t sk[KPL];  // 0 = empty (score keys of non-NaN scores are nonzero)
   uint32_t n_ok = 0;
@@ -67,7 +91,7 @@ __device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const boo
     n_ok += (uint32_t)__popcll(__ballot(ok[q]));
   }
   const uint32_t take = n_ok < m ? n_ok : m;
-  uint64_t key_r = 0ull;
+  uint64_t v = 0ull;
   for (uint32_t r = 0; r < take; ++r) {
     uint32_t lm = 0;
 #pragma unroll
@@ -91,16 +115,14 @@ __device__ __forceinline__ uint32_t wave_top_m(const float (&sc)[KPL], const boo
     for (int q = 0; q < KPL; ++q)
       if (q == oq) ob = blk[q];
     ob = (uint32_t)__builtin_amdgcn_readlane((int)ob, owner);
-    key_r = ((uint64_t)M << 32) | (uint32_t)~ob;
     if (lane == owner) {
 #pragma unroll
       for (int q = 0; q < KPL; ++q)
         if (q == oq) sk[q] = 0u;
-      out[r] = key_r;
     }
+    if (lane == (int)r) v = ((uint64_t)M << 32) | (uint32_t)~ob;
   }
-  for (uint32_t i = take + (uint32_t)lane; i < m; i += 64) out[i] = 0ull;
-  *last = key_r;
+  *val = v;
   return n_ok;
 }
 
@@ -142,7 +164,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // token's blocks are cut into groups of consecutive blocks: one indexer
 // wave's blocks, or with merging one indexer workgroup's.  Group g of token t
 // has list_len composite keys at cand[(t*groups_per_token + g)*list_len],
-// descending and zero-padded, and a bound gcut[t*groups_per_token + g] that
+// zero-padded, and a bound gcut[t*groups_per_token + g] that
 // is >= the key of every block of the group missing from the list (0: the
 // list holds every block of the group).
 constexpr int kIndexWaves = 8;      // waves per indexer workgroup
@@ -155,56 +177,61 @@ struct CandArgs {
   int groups_per_token;
 };
 
-// Candidate-list epilogue.  Lane L of the calling wave holds score ks[q] of
-// block blk[q] where ok[q] (indices ascending in (q, lane) order).  Without
-// merging the wave's top-wave_m keys are its group's list and the group bound
-// is the list's last key when the wave has more valid blocks.  With merging
-// every wave of the workgroup calls this (it holds a barrier): each wave's
-// top-wave_m and bound go to LDS (wave w's kMergeMaxWaveM + 1 words at
+// Publishes a wave's candidate list: lane r < wave_m holds the wave's r-th
+// largest composite key (zero past its valid blocks) and n_ok counts the
+// wave's valid blocks.  Without merging the list is its group's list and the
+// group bound is the list's last key when the wave has more valid blocks.
+// With merging every wave of the workgroup calls this (it holds a barrier):
+// each wave's list and bound go to LDS (wave w's kMergeMaxWaveM + 1 words at
 // lds + w*lds_stride), and wave 0 keeps the list_len largest of those
 // kIndexWaves*wave_m keys.  A block missing from the merged list is either
 // below the largest key left out of it, or missing from its wave's list and
 // so below that wave's last key; the bound is the larger of those.
-template <int KPL>
-__device__ __forceinline__ void cand_epilogue(const float (&ks)[KPL], const bool (&ok)[KPL],
-                                              const uint32_t (&blk)[KPL], const CandArgs& ca,
-                                              int64_t t, int64_t wave_in_token,
-                                              int64_t wg_in_token, uint64_t* lds,
-                                              int lds_stride) {
+__device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const CandArgs& ca,
+                                             int64_t t, int64_t wave_in_token,
+                                             int64_t wg_in_token, uint64_t* lds,
+                                             int lds_stride) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t last;
+  const int m = ca.wave_m;
+  const uint64_t wlast = readlane_u64(val, m - 1);
+  const uint64_t wbound = n_ok > (uint32_t)m ? wlast : 0ull;
   if (!ca.merge) {
     const int64_t g = t * ca.groups_per_token + wave_in_token;
-    const uint32_t n_ok =
-        wave_top_m<KPL>(ks, ok, blk, (uint32_t)ca.wave_m, ca.cand + g * ca.list_len, &last);
-    if (lane == 0) ca.gcut[g] = n_ok > (uint32_t)ca.wave_m ? last : 0ull;
+    if (lane < m) ca.cand[g * ca.list_len + lane] = val;
+    if (lane == 0) ca.gcut[g] = wbound;
     return;
   }
   uint64_t* mine = lds + wave * lds_stride;
-  const uint32_t n_ok = wave_top_m<KPL>(ks, ok, blk, (uint32_t)ca.wave_m, mine, &last);
-  if (lane == 0) mine[kMergeMaxWaveM] = n_ok > (uint32_t)ca.wave_m ? last : 0ull;
+  if (lane < kMergeMaxWaveM) mine[lane] = lane < m ? val : 0ull;
+  if (lane == 0) mine[kMergeMaxWaveM] = wbound;
   __syncthreads();
   if (wave != 0) return;
-  const int m = ca.wave_m;
   const int w = lane / m;
   const uint64_t key = lane < kIndexWaves * m ? lds[w * lds_stride + (lane - w * m)] : 0ull;
-  // rank among the 64 lanes' keys; equal keys (only zeros) rank by lane
-  const uint32_t klo = (uint32_t)key, khi = (uint32_t)(key >> 32);
-  uint32_t rank = 0;
-  for (int j = 0; j < 64; ++j) {
-    const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, j) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)klo, j);
-    rank += (kj > key || (kj == key && j < lane)) ? 1u : 0u;
+  // Rank among the kIndexWaves*m keys (unique where nonzero): the number of
+  // larger keys, read back from LDS by every lane at once (broadcast reads
+  // of every slot; unused slots hold zero); zero keys rank after all nonzero
+  // keys in lane order.
+  uint32_t above = 0;
+#pragma unroll 1
+  for (int v0 = 0; v0 < kIndexWaves; v0 += 2) {  // two waves' slots per batch of reads
+    uint64_t kv[2 * kMergeMaxWaveM];
+#pragma unroll
+    for (int j = 0; j < 2 * kMergeMaxWaveM; ++j)
+      kv[j] = lds[(v0 + j / kMergeMaxWaveM) * lds_stride + j % kMergeMaxWaveM];
+#pragma unroll
+    for (int j = 0; j < 2 * kMergeMaxWaveM; ++j) above += kv[j] > key ? 1u : 0u;
   }
+  const uint64_t zero_lanes = __ballot(key == 0ull);
+  const uint32_t nonzero = 64u - (uint32_t)__popcll(zero_lanes);
+  const uint32_t rank =
+      key != 0ull ? above
+                  : nonzero + (uint32_t)__popcll(zero_lanes & ((1ull << lane) - 1ull));
   const int64_t g = t * ca.groups_per_token + wg_in_token;
   if (rank < (uint32_t)ca.list_len) ca.cand[g * ca.list_len + rank] = key;
+  // the largest key left out of the list, and the waves' own bounds
   const uint64_t out_mask = __ballot(rank == (uint32_t)ca.list_len);
-  uint64_t cut = 0ull;
-  if (out_mask != 0ull) {
-    const int o = __ffsll((unsigned long long)out_mask) - 1;
-    cut = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, o) << 32) |
-          (uint32_t)__builtin_amdgcn_readlane((int)klo, o);
-  }
+  uint64_t cut = out_mask != 0ull ? readlane_u64(key, __ffsll((unsigned long long)out_mask) - 1) : 0ull;
 #pragma unroll
   for (int v = 0; v < kIndexWaves; ++v) {
     const uint64_t wc = lds[v * lds_stride + kMergeMaxWaveM];

@@ -177,14 +177,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   // for the workgroup merge (no DMA into them is pending by then).
   uint64_t* cand_lds = reinterpret_cast<uint64_t*>(&ktile[0][0][0]);
   constexpr int kCandStride = 2 * TILE_CHUNKS * 2;  // u64 words per wave's buffers
-  constexpr int KPL = kMaxTpw / 2;
   if (!active) {
-    if (ca.cand != nullptr) {  // empty list and bound (and the merge barrier)
-      float ks[KPL] = {};
-      bool ok[KPL] = {};
-      uint32_t blk[KPL] = {};
-      cand_epilogue<KPL>(ks, ok, blk, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
-    }
+    if (ca.cand != nullptr)  // empty list and bound (and the merge barrier)
+      cand_publish(0ull, 0u, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
     return;
   }
   u32x4 qv[kQRegs ? MT : 1][KS];
@@ -196,6 +191,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   }
 
   float sc[kMaxTpw];
+  // Running candidate list: lane r < wave_m holds the r-th largest composite
+  // key of the wave's blocks so far (zero beyond them); n_ok counts them.
+  uint64_t rl = 0ull;
+  uint32_t n_ok = 0;
 #pragma unroll
   for (int j = 0; j < kMaxTpw; ++j) {
     sc[j] = 0.0f;
@@ -234,6 +233,44 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       }
       part += __shfl_xor(part, 32);
       sc[j] = part;
+      if (ca.cand != nullptr) {
+        // Merge this tile into the running list (sorted, descending) while
+        // the next tile's DMA is in flight.  Lanes 32..63 hold the tile's
+        // blocks (the same scores as lanes 0..31).
+        const int m = ca.wave_m;
+        const int64_t b = tile * kTileN + col;
+        const bool tv = half == 1 && b < n_vis;
+        const uint32_t tsk = tv ? score_key(part) : 0u;
+        const uint64_t tkey = tsk != 0u ? ((uint64_t)tsk << 32) | (uint32_t)~(uint32_t)b : 0ull;
+        n_ok += (uint32_t)__popcll(__ballot(tv));
+        const uint64_t cut = readlane_u64(rl, m - 1);  // 0 until the list is full
+        uint64_t cmask = __ballot(tkey > cut);
+        const int nc = __popcll(cmask);
+        if (nc > 0 && m <= 16 && nc <= 8) {
+          // few keys beat the list: insert each (lane i takes its own entry,
+          // the key, or the entry above it)
+          while (cmask != 0ull) {
+            const int l = __ffsll((unsigned long long)cmask) - 1;
+            cmask &= cmask - 1ull;
+            const uint64_t k = readlane_u64(tkey, l);
+            const uint64_t prev = row_shr1_u64(rl);  // lane 0 of a row: all ones
+            if (lane < m) rl = rl > k ? rl : (prev > k ? k : prev);
+          }
+        } else if (nc > 0) {
+          // wave_m rounds over the list (lanes 0..31) and the tile (lanes
+          // 32..63): lane order is block order for equal scores
+          uint32_t sk = half == 1 ? tsk : (uint32_t)(rl >> 32);
+          const uint32_t lo = half == 1 ? (uint32_t)tkey : (uint32_t)rl;
+          const uint32_t avail = (uint32_t)__popcll(__ballot(sk != 0u));
+          const uint32_t take = avail < (uint32_t)m ? avail : (uint32_t)m;
+          uint64_t nrl = 0ull;
+          for (uint32_t r = 0; r < take; ++r) {
+            const uint64_t kr = wave_take_max(sk, lo);
+            if (lane == (int)r) nrl = kr;
+          }
+          rl = nrl;
+        }
+      }
     }
   }
 
@@ -246,23 +283,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     if (q < nt && half == 0 && blk < n_vis) srow[blk] = sc[q];
   }
 
-  if (ca.cand != nullptr) {
-    // both half-waves hold every tile's scores: half h takes tiles 2p + h
-    float ks[KPL];
-    bool ok[KPL];
-    uint32_t blk[KPL];
-#pragma unroll
-    for (int p = 0; p < KPL; ++p) {
-      const int q = 2 * p + half;
-      const int64_t b = (tile_begin + q) * kTileN + col;
-      float x0 = sc[2 * p], x1 = sc[2 * p + 1];
-      asm volatile("" : "+v"(x0), "+v"(x1));  // keep sc[] in registers: no indexed load
-      ks[p] = half ? x1 : x0;
-      ok[p] = q < nt && b < n_vis;
-      blk[p] = (uint32_t)b;
-    }
-    cand_epilogue<KPL>(ks, ok, blk, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
-  }
+  if (ca.cand != nullptr)
+    cand_publish(rl, n_ok, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
 }
 
 template <int IHD, int MT>

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
     blk[p] = (uint32_t)b;
     sc[p] = ok[p] ? srow[b] : 0.0f;
   }
-  cand_epilogue<KPH>(sc, ok, blk, ca, t, wave_in_token, blockIdx.x, lds, kStride);
+  uint64_t val;
+  const uint32_t n_ok = wave_top_m<KPH>(sc, ok, blk, (uint32_t)ca.wave_m, &val);
+  cand_publish(val, n_ok, ca, t, wave_in_token, blockIdx.x, lds, kStride);
 }
 
 }  // namespace
