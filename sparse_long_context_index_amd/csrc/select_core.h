@@ -81,7 +81,7 @@ __device__ __forceinline__ void wave_append(bool p, uint64_t v, uint64_t* list, 
   const int leader = __ffsll((unsigned long long)mask) - 1;
   uint32_t base = 0;
   if (lane == leader) base = atomicAdd(n, (uint32_t)__popcll(mask));
-  base = __shfl(base, leader);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
   if (p) {
     const uint32_t o = base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
     if (o < cap) list[o] = v;
@@ -100,12 +100,9 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t (&c)[BPT], uin
   uint32_t tot = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) tot += c[i];
-  uint32_t x = tot;  // inclusive suffix sum within the wave
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_down(x, d);
-    if (lane + d < 64) x += y;
-  }
+  // inclusive suffix sum within the wave
+  const uint32_t pre = wave_incl_scan_u32(tot);
+  const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;
   if (lane == 0) scratch[wave] = x;
   __syncthreads();
   uint32_t acc = x - tot;
@@ -128,12 +125,7 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t (&c)[BPT], uin
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch,
                                                     uint32_t& total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan_u32(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
   uint32_t base = 0;
@@ -259,14 +251,13 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
     ulo = min(ulo, h);
     uhi = max(uhi, h);
   }
-  for (int b = tid; b < kBins; b += kThreads) sh.hist[b] = 0u;
+  static_assert(kBins == 2 * kThreads, "two bins per thread");
+  sh.hist[tid] = 0u;
+  sh.hist[tid + kThreads] = 0u;
   if (tid == 0) sh.n_list = 0u;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    nz += __shfl_xor(nz, off);
-    ulo = min(ulo, (uint32_t)__shfl_xor(ulo, off));
-    uhi = max(uhi, (uint32_t)__shfl_xor(uhi, off));
-  }
+  nz = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_u32(nz), 63);
+  ulo = wave_min_u32(ulo);
+  uhi = wave_max_u32(uhi);
   if (lane == 0) {
     sh.rc[wave] = nz;
     sh.rlo[wave] = ulo;
@@ -298,12 +289,9 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
     // thread i owns bins 2i, 2i+1 ----
     const uint32_t c0 = sh.hist[2 * tid], c1 = sh.hist[2 * tid + 1];
     const uint32_t tot = c0 + c1;
-    uint32_t x = tot;  // inclusive suffix sum within the wave
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_down(x, d);
-      if (lane + d < 64) x += y;
-    }
+    // inclusive suffix sum within the wave
+    const uint32_t pre = wave_incl_scan_u32(tot);
+    const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;
     if (lane == 0) sh.fb_w[wave] = x;
     __syncthreads();
     uint32_t acc = x - tot;
