@@ -88,6 +88,20 @@ __device__ __forceinline__ void wave_append(bool p, uint64_t v, uint64_t* list, 
   }
 }
 
+// Per-wave values vals[0..kWaves) in LDS (one per wave of the workgroup):
+// lane w < kWaves reads value w, so one read and a DPP scan give the sum of
+// the values before this wave's, the sum after it, and the total.
+__device__ __forceinline__ void cross_wave_sums(const uint32_t* vals, uint32_t& before,
+                                                uint32_t& after, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t v = lane < kWaves ? vals[lane] : 0u;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t upto = (uint32_t)__builtin_amdgcn_readlane((int)incl, wave);
+  before = upto - (uint32_t)__builtin_amdgcn_readlane((int)v, wave);
+  after = total - upto;
+}
+
 // Block-wide search in a histogram distributed over the workgroup: thread i
 // owns bins [i*BPT, i*BPT+BPT) in `c`.  Finds the bin b with
 //   (items in bins > b) < need <= (items in bins >= b)
@@ -105,8 +119,9 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t (&c)[BPT], uin
   const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;
   if (lane == 0) scratch[wave] = x;
   __syncthreads();
-  uint32_t acc = x - tot;
-  for (int wv = wave + 1; wv < kWaves; ++wv) acc += scratch[wv];
+  uint32_t before_w, after_w, total_w;
+  cross_wave_sums(scratch, before_w, after_w, total_w);
+  uint32_t acc = x - tot + after_w;
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
     if (acc < need && acc + c[i] >= need) {
@@ -128,12 +143,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
   const uint32_t x = wave_incl_scan_u32(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
-  uint32_t base = 0;
-  total = 0;
-  for (int wv = 0; wv < kWaves; ++wv) {
-    if (wv < wave) base += scratch[wv];
-    total += scratch[wv];
-  }
+  uint32_t base, after;
+  cross_wave_sums(scratch, base, after, total);
   __syncthreads();
   return base + x - v;
 }
@@ -264,12 +275,12 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
     sh.rhi[wave] = uhi;
   }
   __syncthreads();
-  uint32_t n_nz = 0, blo = 0xFFFFFFFFu, bhi = 0u;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    n_nz += sh.rc[w];
-    blo = min(blo, sh.rlo[w]);
-    bhi = max(bhi, sh.rhi[w]);
+  uint32_t n_nz, blo, bhi;
+  {
+    uint32_t before_w, after_w;
+    cross_wave_sums(sh.rc, before_w, after_w, n_nz);
+    blo = wave_min_u32(lane < kWaves ? sh.rlo[lane] : 0xFFFFFFFFu);
+    bhi = wave_max_u32(lane < kWaves ? sh.rhi[lane] : 0u);
   }
   if (n_nz < k) return 0ull;
   const uint32_t range = bhi - blo;
@@ -294,8 +305,9 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
     const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + tot;
     if (lane == 0) sh.fb_w[wave] = x;
     __syncthreads();
-    uint32_t acc = x - tot;
-    for (int wv = wave + 1; wv < kWaves; ++wv) acc += sh.fb_w[wv];
+    uint32_t before_w, after_w, total_w;
+    cross_wave_sums(sh.fb_w, before_w, after_w, total_w);
+    uint32_t acc = x - tot + after_w;
     if (acc < k && acc + c1 >= k) {
       sh.fb_bin = 2u * tid + 1u;
       sh.fb_above = acc;
@@ -436,7 +448,9 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
   uint64_t gc[2];
   if (CT > 0u) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) key[i] = cand[min((uint32_t)tid + (uint32_t)i * kThreads, CT - 1u)];
+    for (int i = 0; i < KPT; ++i)
+      key[i] = (uint32_t)i * kThreads < CT ? cand[min((uint32_t)tid + (uint32_t)i * kThreads, CT - 1u)]
+                                           : 0ull;
 #pragma unroll
     for (int i = 0; i < 2; ++i) gc[i] = gcut[min((uint32_t)tid + (uint32_t)i * kThreads, NG - 1u)];
 #pragma unroll
