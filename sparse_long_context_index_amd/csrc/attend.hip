@@ -28,6 +28,8 @@
 // gathered here (selected compressed rows through their block indices, then
 // the SWA rows) and copied into all_kv while they are staged, which fuses the
 // gather stage into the attention.
+#include <type_traits>
+
 #include "select_core.h"
 
 namespace csa {
@@ -148,13 +150,18 @@ struct alignas(16) AttSmem {
 // 0-3 run the products and the softmax (the others only join the barriers).
 // Q comes from registers (qa) or from LDS (qlds, 16 rows of D+8); in gather
 // mode the block index of row rr comes from a prefetch of sel_idx (pidx holds
-// the first tile's) or, when SEL_LDS, from selrow[rr - row_begin].
+// the first tile's) or, when SEL_LDS, from selrow[rr - row_begin].  With
+// SEL_LDS the first tile is staged straight from the whole selection in LDS
+// (sel_first[rr], or rr itself when sel_first is null), before the barrier
+// after which that LDS (aliased by sm) may be overwritten: its loads are in
+// flight across the barrier.
 template <int D, int MODE, bool HAS_B, int NT, bool Q_LDS, bool SEL_LDS>
 __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& sm, int t,
                                              int split, int n_splits, int row_begin, int row_end,
                                              const SegDesc& sd, int32_t pidx,
-                                             const int32_t* selrow, const bf16x8 (&qa)[D / 32],
-                                             const uint16_t* qlds, bool copy_rows) {
+                                             const int32_t* selrow, const int32_t* sel_first,
+                                             const bf16x8 (&qa)[D / 32], const uint16_t* qlds,
+                                             bool copy_rows) {
   constexpr bool kGather = MODE == kModeGather;
   using L = Layout<D>;
   constexpr int KSQ = D / 32;  // k-steps of S^T = K Q^T
@@ -176,174 +183,203 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
 
   const uint16_t* kv_a = p.kv_a;
   const uint16_t* kv_b = p.kv_b;
-  for (int r0 = row_begin; r0 < row_end; r0 += kRT) {
-    __syncthreads();  // the previous tile has been consumed
-    // ---- row sources of this tile: one thread per row resolves the block
-    // index (gather mode) or segment B, into an LDS table ----
-    if (tid < kRT) {
-      const int rr = r0 + tid;
-      int64_t src = -1;
-      if (rr < row_end) {
-        if (rr < sd.alen) {
-          int64_t ar = sd.a0 + rr;
-          if constexpr (kGather) {
-            ar = sd.a0 + (SEL_LDS ? selrow[rr - row_begin] : pidx);
-            if (ar < 0 || ar >= p.a_rows) {
-              flags |= CSA_DERR_ROW_RANGE;
-              ar = -1;
+  // One tile; the first tile of a SEL_LDS call is staged directly (see above).
+  auto tile = [&](auto direct_tag, const int r0) {
+    constexpr bool direct = decltype(direct_tag)::value;
+      if constexpr (!direct) {
+        __syncthreads();  // the previous tile has been consumed
+        // ---- row sources of this tile: one thread per row resolves the block
+        // index (gather mode) or segment B, into an LDS table ----
+        if (tid < kRT) {
+          const int rr = r0 + tid;
+          int64_t src = -1;
+          if (rr < row_end) {
+            if (rr < sd.alen) {
+              int64_t ar = sd.a0 + rr;
+              if constexpr (kGather) {
+                ar = sd.a0 + (SEL_LDS ? selrow[rr - row_begin] : pidx);
+                if (ar < 0 || ar >= p.a_rows) {
+                  flags |= CSA_DERR_ROW_RANGE;
+                  ar = -1;
+                }
+              }
+              src = ar < 0 ? -1 : ar * D;
+            } else {
+              src = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
             }
           }
-          src = ar < 0 ? -1 : ar * D;
-        } else {
-          src = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
+          sm.rsrc[tid] = src;
+          // prefetch the next tile's block indices
+          if (kGather && !SEL_LDS && r0 + kRT < row_end)
+            pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(r0 + kRT + tid, p.sel_stride - 1)];
+        }
+        __syncthreads();
+      }
+      // ---- stage the tile.  The P V product takes its 32 rows per k-step in
+      // the order the S^T accumulators hold them, so 8-row group g = 4*kp + qg
+      // is rows 32*kp + 16*(j/4) + 4*qg + j%4, j < 8.  Each thread loads one
+      // 8x8 (rows x d) block of a group, writes it row-major (A operand of S^T)
+      // and transposed (A operand of O^T), and (head group 0) copies it to
+      // all_kv. ----
+      constexpr int NB = (kRT / 8) * DP;     // 8x8 blocks per tile
+      constexpr int BPTH = (NB + NT - 1) / NT;  // blocks per thread
+      u32x4 rows[BPTH][8];
+  #pragma unroll
+      for (int q = 0; q < BPTH; ++q) {
+        const int b = tid + q * NT;
+        const int g = b / DP, dp = b - g * DP;
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
+          int64_t src = -1;
+          if constexpr (direct) {
+            const int rr = r0 + row;
+            if (b < NB && rr < row_end) {
+              if (rr < sd.alen) {
+                const int64_t ar = sd.a0 + (sel_first != nullptr ? sel_first[rr] : rr);
+                if (ar < 0 || ar >= p.a_rows)
+                  flags |= CSA_DERR_ROW_RANGE;
+                else
+                  src = ar * D;
+              } else {
+                src = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
+              }
+            }
+          } else if (b < NB) {
+            src = sm.rsrc[row];
+          }
+          rows[q][k] = u32x4{0u, 0u, 0u, 0u};
+          if (src >= 0) {
+            const uint16_t* base = (src & kSegB) ? kv_b : kv_a;
+            rows[q][k] = *reinterpret_cast<const u32x4*>(base + (src & ~kSegB) + dp * 8);
+          }
         }
       }
-      sm.rsrc[tid] = src;
-      // prefetch the next tile's block indices
-      if (kGather && !SEL_LDS && r0 + kRT < row_end)
-        pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(r0 + kRT + tid, p.sel_stride - 1)];
-    }
-    __syncthreads();
-    // ---- stage the tile.  The P V product takes its 32 rows per k-step in
-    // the order the S^T accumulators hold them, so 8-row group g = 4*kp + qg
-    // is rows 32*kp + 16*(j/4) + 4*qg + j%4, j < 8.  Each thread loads one
-    // 8x8 (rows x d) block of a group, writes it row-major (A operand of S^T)
-    // and transposed (A operand of O^T), and (head group 0) copies it to
-    // all_kv. ----
-    constexpr int NB = (kRT / 8) * DP;     // 8x8 blocks per tile
-    constexpr int BPTH = (NB + NT - 1) / NT;  // blocks per thread
-    u32x4 rows[BPTH][8];
-#pragma unroll
-    for (int q = 0; q < BPTH; ++q) {
-      const int b = tid + q * NT;
-      const int g = b / DP, dp = b - g * DP;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
-        const int64_t src = b < NB ? sm.rsrc[row] : -1;
-        rows[q][k] = u32x4{0u, 0u, 0u, 0u};
-        if (src >= 0) {
-          const uint16_t* base = (src & kSegB) ? kv_b : kv_a;
-          rows[q][k] = *reinterpret_cast<const u32x4*>(base + (src & ~kSegB) + dp * 8);
+      if constexpr (direct) __syncthreads();  // the selection's LDS may be overwritten from here
+  #pragma unroll
+      for (int q = 0; q < BPTH; ++q) {
+        const int b = tid + q * NT;
+        if (b >= NB) break;
+        const int g = b / DP, dp = b - g * DP;
+  #pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
+          *reinterpret_cast<u32x4*>(&sm.rm[row * L::RM + dp * 8]) = rows[q][k];
+          if (copy_rows && r0 + row < row_end)
+            *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + r0 + row) * D +
+                                      dp * 8) = rows[q][k];
+        }
+        uint16_t* ilg = &sm.il[g * L::ILG + dp * 8 * 8 + dp * 8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const int wi = e >> 1;
+          u32x4 c;
+          c.x = perm(rows[q][1][wi], rows[q][0][wi], sel);
+          c.y = perm(rows[q][3][wi], rows[q][2][wi], sel);
+          c.z = perm(rows[q][5][wi], rows[q][4][wi], sel);
+          c.w = perm(rows[q][7][wi], rows[q][6][wi], sel);
+          *reinterpret_cast<u32x4*>(ilg + e * 8) = c;
         }
       }
-    }
-#pragma unroll
-    for (int q = 0; q < BPTH; ++q) {
-      const int b = tid + q * NT;
-      if (b >= NB) break;
-      const int g = b / DP, dp = b - g * DP;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
-        *reinterpret_cast<u32x4*>(&sm.rm[row * L::RM + dp * 8]) = rows[q][k];
-        if (copy_rows && r0 + row < row_end)
-          *reinterpret_cast<u32x4*>(p.copy_out + ((int64_t)t * p.copy_stride + r0 + row) * D +
-                                    dp * 8) = rows[q][k];
-      }
-      uint16_t* ilg = &sm.il[g * L::ILG + dp * 8 * 8 + dp * 8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int wi = e >> 1;
-        u32x4 c;
-        c.x = perm(rows[q][1][wi], rows[q][0][wi], sel);
-        c.y = perm(rows[q][3][wi], rows[q][2][wi], sel);
-        c.z = perm(rows[q][5][wi], rows[q][4][wi], sel);
-        c.w = perm(rows[q][7][wi], rows[q][6][wi], sel);
-        *reinterpret_cast<u32x4*>(ilg + e * 8) = c;
-      }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    float x[4];
-    if (mma) {
-      // ---- S^T = K Q^T for this wave's 16 tile rows x the 16 heads.  The
-      // fragments of k-step ks+1 are read from LDS while the MFMA of ks runs.
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = &sm.rm[(wave * 16 + li) * L::RM + quad * 8];
-      const uint16_t* qrow = qlds + li * (D + 8) + quad * 8;
-      bf16x8 kb[2], qb[2];
-      kb[0] = *reinterpret_cast<const bf16x8*>(krow);
-      if constexpr (Q_LDS) qb[0] = *reinterpret_cast<const bf16x8*>(qrow);
-#pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) {
-        if (ks + 1 < KSQ) {
-          kb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(krow + (ks + 1) * 32);
-          if constexpr (Q_LDS) qb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(qrow + (ks + 1) * 32);
+      float x[4];
+      if (mma) {
+        // ---- S^T = K Q^T for this wave's 16 tile rows x the 16 heads.  The
+        // fragments of k-step ks+1 are read from LDS while the MFMA of ks runs.
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* krow = &sm.rm[(wave * 16 + li) * L::RM + quad * 8];
+        const uint16_t* qrow = qlds + li * (D + 8) + quad * 8;
+        bf16x8 kb[2], qb[2];
+        kb[0] = *reinterpret_cast<const bf16x8*>(krow);
+        if constexpr (Q_LDS) qb[0] = *reinterpret_cast<const bf16x8*>(qrow);
+  #pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+          if (ks + 1 < KSQ) {
+            kb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(krow + (ks + 1) * 32);
+            if constexpr (Q_LDS) qb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(qrow + (ks + 1) * 32);
+          }
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1], Q_LDS ? qb[ks & 1] : qa[ks], s, 0,
+                                                      0, 0);
         }
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[ks & 1], Q_LDS ? qb[ks & 1] : qa[ks], s, 0,
-                                                    0, 0);
-      }
-      // s[r] = S[head h][tile row wave*16 + 4*quad + r]
-      // ---- online softmax (exp2 domain): per-wave maxima over 16 rows, then
-      // the tile maximum of each head through LDS ----
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool valid = r0 + wave * 16 + 4 * quad + r < row_end;
-        x[r] = valid ? s[r] * sl2 : -INFINITY;
-        mloc = fmaxf(mloc, x[r]);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      if (quad == 0) sm.red_m[wave][li] = mloc;
-    }
-    __syncthreads();
-    float alpha = 1.f;
-    if (mma) {
-      const float mtile = fmaxf(fmaxf(sm.red_m[0][li], sm.red_m[1][li]),
-                                fmaxf(sm.red_m[2][li], sm.red_m[3][li]));
-      const float mnew = fmaxf(m_run, mtile);
-      alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run - mnew);
-      float lsum = 0.f;
-      float pv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[r] = (x[r] == -INFINITY) ? 0.f : exp2f(x[r] - mnew);
-        lsum += pv[r];
-      }
-      lsum += __shfl_xor(lsum, 16);
-      lsum += __shfl_xor(lsum, 32);
-      // P[head li][tile rows wave*16 + 4*quad .. +4] as bf16
-      *reinterpret_cast<uint2*>(&sm.pl[li * kRT + wave * 16 + 4 * quad]) =
-          make_uint2((uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16),
-                     (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16));
-      if (quad == 0) sm.red_l[wave][li] = lsum;
-      m_run = mnew;
-    }
-    __syncthreads();
-    if (mma) {
-      l_run = l_run * alpha +
-              (sm.red_l[0][li] + sm.red_l[1][li] + sm.red_l[2][li] + sm.red_l[3][li]);
-#pragma unroll
-      for (int n = 0; n < NTW; ++n) o[n] *= alpha;
-      // P^T (B operand of O^T) for k-step kp: rows 32kp + 4*quad + 0..3 and
-      // 32kp + 16 + 4*quad + 0..3 of head li
-      bf16x8 pb[2];
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(&sm.pl[li * kRT + 32 * kp + 4 * quad]);
-        const uint2 hi =
-            *reinterpret_cast<const uint2*>(&sm.pl[li * kRT + 32 * kp + 16 + 4 * quad]);
-        pb[kp] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-      }
-      // ---- O^T += V^T P^T for this wave's quarter of D ----
-#pragma unroll
-      for (int kp = 0; kp < kRT / 32; ++kp) {
-        const uint16_t* ilg = &sm.il[(kp * 4 + quad) * L::ILG];
-        bf16x8 vb[NTW];
-#pragma unroll
-        for (int nn = 0; nn < NTW; ++nn) {
-          const int d = (wave * NTW + nn) * 16 + li;
-          vb[nn] = *reinterpret_cast<const bf16x8*>(ilg + d * 8 + (d >> 3) * 8);
+        // s[r] = S[head h][tile row wave*16 + 4*quad + r]
+        // ---- online softmax (exp2 domain): per-wave maxima over 16 rows, then
+        // the tile maximum of each head through LDS ----
+        float mloc = -INFINITY;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool valid = r0 + wave * 16 + 4 * quad + r < row_end;
+          x[r] = valid ? s[r] * sl2 : -INFINITY;
+          mloc = fmaxf(mloc, x[r]);
         }
-#pragma unroll
-        for (int nn = 0; nn < NTW; ++nn)
-          o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[nn], pb[kp], o[nn], 0, 0, 0);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        if (quad == 0) sm.red_m[wave][li] = mloc;
       }
+      __syncthreads();
+      float alpha = 1.f;
+      if (mma) {
+        const float mtile = fmaxf(fmaxf(sm.red_m[0][li], sm.red_m[1][li]),
+                                  fmaxf(sm.red_m[2][li], sm.red_m[3][li]));
+        const float mnew = fmaxf(m_run, mtile);
+        alpha = (mnew == -INFINITY) ? 1.f : exp2f(m_run - mnew);
+        float lsum = 0.f;
+        float pv[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[r] = (x[r] == -INFINITY) ? 0.f : exp2f(x[r] - mnew);
+          lsum += pv[r];
+        }
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        // P[head li][tile rows wave*16 + 4*quad .. +4] as bf16
+        *reinterpret_cast<uint2*>(&sm.pl[li * kRT + wave * 16 + 4 * quad]) =
+            make_uint2((uint32_t)f32_to_bf16(pv[0]) | ((uint32_t)f32_to_bf16(pv[1]) << 16),
+                       (uint32_t)f32_to_bf16(pv[2]) | ((uint32_t)f32_to_bf16(pv[3]) << 16));
+        if (quad == 0) sm.red_l[wave][li] = lsum;
+        m_run = mnew;
+      }
+      __syncthreads();
+      if (mma) {
+        l_run = l_run * alpha +
+                (sm.red_l[0][li] + sm.red_l[1][li] + sm.red_l[2][li] + sm.red_l[3][li]);
+  #pragma unroll
+        for (int n = 0; n < NTW; ++n) o[n] *= alpha;
+        // P^T (B operand of O^T) for k-step kp: rows 32kp + 4*quad + 0..3 and
+        // 32kp + 16 + 4*quad + 0..3 of head li
+        bf16x8 pb[2];
+  #pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(&sm.pl[li * kRT + 32 * kp + 4 * quad]);
+          const uint2 hi =
+              *reinterpret_cast<const uint2*>(&sm.pl[li * kRT + 32 * kp + 16 + 4 * quad]);
+          pb[kp] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        }
+        // ---- O^T += V^T P^T for this wave's quarter of D ----
+  #pragma unroll
+        for (int kp = 0; kp < kRT / 32; ++kp) {
+          const uint16_t* ilg = &sm.il[(kp * 4 + quad) * L::ILG];
+          bf16x8 vb[NTW];
+  #pragma unroll
+          for (int nn = 0; nn < NTW; ++nn) {
+            const int d = (wave * NTW + nn) * 16 + li;
+            vb[nn] = *reinterpret_cast<const bf16x8*>(ilg + d * 8 + (d >> 3) * 8);
+          }
+  #pragma unroll
+          for (int nn = 0; nn < NTW; ++nn)
+            o[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[nn], pb[kp], o[nn], 0, 0, 0);
+        }
+      }
+  };
+  int r0 = row_begin;
+  if constexpr (SEL_LDS) {
+    if (r0 < row_end) {
+      tile(std::true_type{}, r0);
+      r0 += kRT;
     }
   }
+  for (; r0 < row_end; r0 += kRT) tile(std::false_type{}, r0);
 
   report(p.err, flags);
   // ---- epilogue: lane (li, quad) of wave w holds d = (w*NTW + nn)*16 +
@@ -425,7 +461,8 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const bool copy_rows = kGather && p.copy_out != nullptr && blockIdx.y == 0;
   attend_tiles<D, MODE, HAS_B, 256, false, false>(p, sm, t, split, n_splits, row_begin, row_end,
-                                                  sd, pidx, nullptr, qa, nullptr, copy_rows);
+                                                  sd, pidx, nullptr, nullptr, qa, nullptr,
+                                                  copy_rows);
 }
 
 // Select and attend in one kernel (decode step, CSA).  Every workgroup of
@@ -486,7 +523,9 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
     const int hl = tid / QPR;
     *reinterpret_cast<u32x4*>(&qlds[hl * (D + 8) + (tid - hl * QPR) * 8]) = qv;
   }
-  for (int i = tid; i < tiles_per_split * kRT; i += kFuseThreads) {
+  // block indices of the split's later tiles (the first is staged straight
+  // from the selection)
+  for (int i = kRT + tid; i < tiles_per_split * kRT; i += kFuseThreads) {
     const uint32_t rr = (uint32_t)(row_begin + i);
     selrow[i] = rr < r.emitted ? (r.listed ? u.s.outl[rr] : (int32_t)rr) : 0;
   }
@@ -507,9 +546,11 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const bool copy_rows = p.copy_out != nullptr && blockIdx.y == 0;
   const bf16x8 qa_unused[KSQ] = {};
-  // attend_tiles starts with a barrier: the select's LDS is free after it
+  // attend_tiles issues the first tile's loads from the selection in LDS,
+  // then waits for every thread before reusing that LDS
   attend_tiles<D, kModeGather, HAS_B, kFuseThreads, true, true>(
-      p, u.a, t, split, n_splits, row_begin, row_end, sd, 0, selrow, qa_unused, qlds, copy_rows);
+      p, u.a, t, split, n_splits, row_begin, row_end, sd, 0, selrow,
+      r.listed ? u.s.outl : nullptr, qa_unused, qlds, copy_rows);
 }
 
 // Merge of the split partials of one (token, head).  Wave w takes splits
