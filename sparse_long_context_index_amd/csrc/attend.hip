@@ -150,16 +150,15 @@ struct alignas(16) AttSmem {
 // 0-3 run the products and the softmax (the others only join the barriers).
 // Q comes from registers (qa) or from LDS (qlds, 16 rows of D+8); in gather
 // mode the block index of row rr comes from a prefetch of sel_idx (pidx holds
-// the first tile's) or, when SEL_LDS, from selrow[rr - row_begin].  With
-// SEL_LDS the first tile is staged straight from the whole selection in LDS
-// (sel_first[rr], or rr itself when sel_first is null), before the barrier
-// after which that LDS (aliased by sm) may be overwritten: its loads are in
-// flight across the barrier.
+// the first tile's) or, when SEL_LDS, from selrow[rr - row_begin] (rr itself
+// when sel_listed is false: every visible block is selected).  With SEL_LDS
+// the first tile's loads are issued before the tile loop's first barrier, so
+// that they are in flight across it.
 template <int D, int MODE, bool HAS_B, int NT, bool Q_LDS, bool SEL_LDS>
 __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& sm, int t,
                                              int split, int n_splits, int row_begin, int row_end,
                                              const SegDesc& sd, int32_t pidx,
-                                             const int32_t* selrow, const int32_t* sel_first,
+                                             const int32_t* selrow, bool sel_listed,
                                              const bf16x8 (&qa)[D / 32], const uint16_t* qlds,
                                              bool copy_rows) {
   constexpr bool kGather = MODE == kModeGather;
@@ -197,7 +196,7 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
             if (rr < sd.alen) {
               int64_t ar = sd.a0 + rr;
               if constexpr (kGather) {
-                ar = sd.a0 + (SEL_LDS ? selrow[rr - row_begin] : pidx);
+                ar = sd.a0 + (SEL_LDS ? (sel_listed ? selrow[rr - row_begin] : rr) : pidx);
                 if (ar < 0 || ar >= p.a_rows) {
                   flags |= CSA_DERR_ROW_RANGE;
                   ar = -1;
@@ -236,7 +235,7 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
             const int rr = r0 + row;
             if (b < NB && rr < row_end) {
               if (rr < sd.alen) {
-                const int64_t ar = sd.a0 + (sel_first != nullptr ? sel_first[rr] : rr);
+                const int64_t ar = sd.a0 + (sel_listed ? selrow[rr - row_begin] : rr);
                 if (ar < 0 || ar >= p.a_rows)
                   flags |= CSA_DERR_ROW_RANGE;
                 else
@@ -255,7 +254,7 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
           }
         }
       }
-      if constexpr (direct) __syncthreads();  // the selection's LDS may be overwritten from here
+      if constexpr (direct) __syncthreads();  // the select's LDS (aliased by sm) is free from here
   #pragma unroll
       for (int q = 0; q < BPTH; ++q) {
         const int b = tid + q * NT;
@@ -461,7 +460,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const bool copy_rows = kGather && p.copy_out != nullptr && blockIdx.y == 0;
   attend_tiles<D, MODE, HAS_B, 256, false, false>(p, sm, t, split, n_splits, row_begin, row_end,
-                                                  sd, pidx, nullptr, nullptr, qa, nullptr,
+                                                  sd, pidx, nullptr, false, qa, nullptr,
                                                   copy_rows);
 }
 
@@ -469,10 +468,10 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
 // token t -- one per (row split, 16-head group) -- first runs the token's
 // exact top-k (the 1024-thread select of select_core.h, repeated by each
 // workgroup so that no kernel boundary or global handoff separates the two
-// stages), then keeps the selected block indices of its own rows in LDS and
+// stages), which lists the selected block indices of its own rows in LDS, and
 // runs the tile loop over them and the SWA rows.  The select's LDS is reused
-// for the tiles.  Workgroup (0, 0) of each token writes the token's idx row
-// and count.
+// for the tiles.  The head-group-0 workgroups write the idx entries of their
+// rows; split 0 writes the count.
 constexpr int kFuseThreads = sel::kThreads;
 constexpr int kFuseMaxTiles = 4;  // tiles per split the fused kernel takes
 
@@ -513,29 +512,29 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
     meta.b_len = p.b_len[t];
   }
 
+  const uint32_t win = (uint32_t)(tiles_per_split * kRT);  // this split's rows
   const sel::SelResult r = sel::select_token(
       sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.top_k,
       sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
-      sl.blocks_per_group, u.s);
+      sl.blocks_per_group, u.s, selrow, (uint32_t)row_begin, (uint32_t)row_begin + win);
 
   if (tid < kHeadsPerWg * QPR) {
     const int hl = tid / QPR;
     *reinterpret_cast<u32x4*>(&qlds[hl * (D + 8) + (tid - hl * QPR) * 8]) = qv;
   }
-  // block indices of the split's later tiles (the first is staged straight
-  // from the selection)
-  for (int i = kRT + tid; i < tiles_per_split * kRT; i += kFuseThreads) {
-    const uint32_t rr = (uint32_t)(row_begin + i);
-    selrow[i] = rr < r.emitted ? (r.listed ? u.s.outl[rr] : (int32_t)rr) : 0;
-  }
   meta.a_cnt = (int32_t)r.emitted;
   uint32_t flags = 0;
   const SegDesc sd = token_rows<kModeGather, HAS_B>(p, meta, flags);
-  if (split == 0 && blockIdx.y == 0) {
+  if (blockIdx.y == 0) {
+    // idx entries [row_begin, row_begin + win) below top_k: the selection,
+    // then -1
     int32_t* out = sl.idx + (int64_t)t * sl.top_k;
-    for (uint32_t i = tid; i < (uint32_t)sl.top_k; i += kFuseThreads)
-      out[i] = i < r.emitted ? (r.listed ? u.s.outl[i] : (int32_t)i) : -1;
+    const uint32_t i = (uint32_t)row_begin + (uint32_t)tid;
+    if ((uint32_t)tid < win && i < (uint32_t)sl.top_k)
+      out[i] = i < r.emitted ? (r.listed ? selrow[tid] : (int32_t)i) : -1;
+  }
+  if (split == 0 && blockIdx.y == 0) {
     if (tid == 0) {
       sl.count[t] = (int32_t)r.emitted;
       report(p.err, flags | r.flags);
@@ -546,11 +545,9 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
   const bool copy_rows = p.copy_out != nullptr && blockIdx.y == 0;
   const bf16x8 qa_unused[KSQ] = {};
-  // attend_tiles issues the first tile's loads from the selection in LDS,
-  // then waits for every thread before reusing that LDS
   attend_tiles<D, kModeGather, HAS_B, kFuseThreads, true, true>(
-      p, u.a, t, split, n_splits, row_begin, row_end, sd, 0, selrow,
-      r.listed ? u.s.outl : nullptr, qa_unused, qlds, copy_rows);
+      p, u.a, t, split, n_splits, row_begin, row_end, sd, 0, selrow, r.listed, qa_unused, qlds,
+      copy_rows);
 }
 
 // Merge of the split partials of one (token, head).  Wave w takes splits

@@ -363,11 +363,14 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
 
 // Marks {block of key : key >= thr, key != 0} of the keys in registers, the
 // LDS extras and (if any) the row, in the bitmap (already clear on entry),
-// then lists them in ascending block order at sh.outl[0..top_k); returns how
+// then lists those at positions [e_lo, e_hi) of the ascending block order at
+// dst[0..e_hi-e_lo) (positions below top_k only); returns how
 // many were marked.
 template <class Mark>
 __device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int top_k,
-                                                SelShared& sh) {
+                                                SelShared& sh, int32_t* dst, uint32_t e_lo,
+                                                uint32_t e_hi) {
+  if (e_hi > (uint32_t)top_k) e_hi = (uint32_t)top_k;
   const int tid = threadIdx.x;
   uint32_t emitted = 0;
   const int64_t span = (int64_t)kBitmapWords * 32;
@@ -395,14 +398,22 @@ __device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int to
     for (int q = 0; q < WPT; ++q) mine += (uint32_t)__popc(wv[q]);
     uint32_t sweep_total;
     uint32_t o = emitted + block_excl_scan(mine, sh.scratch, sweep_total);
+    if (o < e_hi && o + mine > e_lo) {  // this thread's bits reach the window
 #pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      uint32_t bits = wv[q];
-      while (bits) {
-        const int bb = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        if (o < (uint32_t)top_k) sh.outl[o] = (int32_t)(base + (int64_t)(tid * WPT + q) * 32 + bb);
-        ++o;
+      for (int q = 0; q < WPT; ++q) {
+        uint32_t bits = wv[q];
+        const uint32_t c = (uint32_t)__popc(bits);
+        if (o < e_hi && o + c > e_lo) {
+          while (bits) {
+            const int bb = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            if (o >= e_lo && o < e_hi)
+              dst[o - e_lo] = (int32_t)(base + (int64_t)(tid * WPT + q) * 32 + bb);
+            ++o;
+          }
+        } else {
+          o += c;
+        }
       }
     }
     emitted += sweep_total;
@@ -418,7 +429,7 @@ __device__ __forceinline__ void mark_block(uint64_t c, int64_t base, int64_t len
 
 struct SelResult {
   uint32_t emitted;  // selected blocks (<= top_k)
-  bool listed;       // the selection is sh.outl[0..emitted); otherwise blocks 0..emitted-1
+  bool listed;       // the selection's window is in dst; otherwise the blocks are 0..emitted-1
   uint32_t flags;    // CSA_DERR_* found in the token's metadata
 };
 
@@ -427,14 +438,16 @@ struct SelResult {
 // arguments.  `cand`/`gcut` are the token's candidate lists and group bounds
 // (list_len keys per group of blocks_per_group blocks, groups_per_token
 // groups; list_len == 0 means none).  On return (after a barrier) the
-// selection is described by the result and, when listed, by sh.outl in
-// ascending block order.
+// selection is described by the result and, when listed, by dst: the blocks
+// at positions [e_lo, e_hi) of the ascending selection, dst[i] holding
+// position e_lo + i (positions at or past the count are not written).
 __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow, int64_t ld,
                                                   int64_t pos_t, int32_t ncomp_t, int ratio,
                                                   int top_k, const uint64_t* __restrict__ cand,
                                                   const uint64_t* __restrict__ gcut, int list_len,
                                                   int groups_per_token, int blocks_per_group,
-                                                  SelShared& sh) {
+                                                  SelShared& sh, int32_t* dst, uint32_t e_lo,
+                                                  uint32_t e_hi) {
   const int tid = threadIdx.x;
   // The candidate lists do not depend on the row length, so they are loaded
   // before it is known: every list of the token (empty groups have zero keys)
@@ -593,7 +606,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
         for (uint32_t j = tid; j < n_x; j += kThreads)
           if (sh.xk[j] >= thr) mark_block(sh.xk[j], base, len, sh);
       };
-      res.emitted = emit_bitmap(mark, n_vis, top_k, sh);
+      res.emitted = emit_bitmap(mark, n_vis, top_k, sh, dst, e_lo, e_hi);
     } else {
       auto getg = [&](uint32_t j) { return block_key(srow[j], j); };
       const uint64_t tg = radix_kth(getg, (uint32_t)n_vis, k_eff, sh);
@@ -603,7 +616,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
           if (c >= tg) mark_block(c, base, len, sh);
         }
       };
-      res.emitted = emit_bitmap(mark, n_vis, top_k, sh);
+      res.emitted = emit_bitmap(mark, n_vis, top_k, sh, dst, e_lo, e_hi);
     }
   }
   if (res.emitted > (uint32_t)top_k) res.emitted = (uint32_t)top_k;

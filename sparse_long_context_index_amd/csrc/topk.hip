@@ -23,7 +23,7 @@ __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
   const sel::SelResult r = sel::select_token(
       scores + (int64_t)t * ld, ld, pos[t], n_comp[t], ratio, top_k,
       cand_all + (int64_t)t * groups_per_token * list_len, gcut_all + (int64_t)t * groups_per_token,
-      list_len, groups_per_token, blocks_per_group, sh);
+      list_len, groups_per_token, blocks_per_group, sh, sh.outl, 0u, (uint32_t)top_k);
   // one coalesced pass writes the selection and the -1 padding
   int32_t* out = idx + (int64_t)t * top_k;
   for (uint32_t i = tid; i < (uint32_t)top_k; i += sel::kThreads)
