@@ -246,14 +246,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
         const uint64_t cut = readlane_u64(rl, m - 1);  // 0 until the list is full
         uint64_t cmask = __ballot(tkey > cut);
         const int nc = __popcll(cmask);
-        if (nc > 0 && m <= 16 && nc <= 8) {
+        if (nc > 0 && nc <= 8) {
           // few keys beat the list: insert each (lane i takes its own entry,
-          // the key, or the entry above it)
+          // the key, or the entry above it; m <= 32, so only lane 16 needs
+          // its upper neighbour from another row)
           while (cmask != 0ull) {
             const int l = __ffsll((unsigned long long)cmask) - 1;
             cmask &= cmask - 1ull;
             const uint64_t k = readlane_u64(tkey, l);
-            const uint64_t prev = row_shr1_u64(rl);  // lane 0 of a row: all ones
+            uint64_t prev = row_shr1_u64(rl);  // lane 0 of a row: all ones
+            const uint64_t r15 = readlane_u64(rl, 15);
+            if (lane == 16) prev = r15;
             if (lane < m) rl = rl > k ? rl : (prev > k ? k : prev);
           }
         } else if (nc > 0) {

@@ -347,6 +347,18 @@ def test_decode_step_batched(dev):
     _check_step(inp, res)
 
 
+@pytest.mark.parametrize("n_seq", [4, 8])
+def test_decode_step_small_batch_multitile(dev, n_seq):
+    """Small batches of long rows take the fused select-and-attend kernel with
+    several 64-row tiles per split (1152 rows over 64 heads: 2 tiles per split
+    at 4 tokens, 3 at 8), so the later tiles read their block indices from the
+    workgroup's window of the selection."""
+    say(f"csa_decode_step small batch: {n_seq} sequences of 64K..80K tokens")
+    inp = gen.batched(5, n_seq=n_seq, lo=65536, hi=81920)
+    res = B().run_decode_step(inp, dev)
+    _check_step(inp, res)
+
+
 def test_decode_step_prefill_sampled(dev):
     say("csa_decode_step prefill chunk: 4096 tokens at 61,440..65,535 (sampled check)")
     inp = gen.prefill()
