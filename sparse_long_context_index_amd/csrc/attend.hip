@@ -602,9 +602,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int
   };
   load_round(0);
 
-  float M = l_s > 0.f ? m_s : -INFINITY;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float M = wave_max_f32(l_s > 0.f ? m_s : -INFINITY);
   if (lane == 0) wred[0][wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
@@ -615,9 +613,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int
   }
   const float f = (l_s > 0.f) ? exp2f(m_s - M) : 0.f;
   fw[tid] = f;
-  float Lp = l_s * f;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) Lp += __shfl_xor(Lp, off);
+  const float Lp = wave_sum_f32(l_s * f);
   if (lane == 0) wred[1][wave] = Lp;
   __syncthreads();
   float Lsum = wred[1][0] + wred[1][1] + wred[1][2] + wred[1][3];

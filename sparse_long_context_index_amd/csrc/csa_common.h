@@ -83,6 +83,38 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// Largest and summed float over the wave, in lane 63 (as wave_max_u32: DPP
+// quad swaps, half-row and row mirrors, then row broadcasts; each step's
+// neutral value fills the rows a broadcast does not write).
+__device__ __forceinline__ float dpp_f32(float old, float v, int ctrl, int row_mask) {
+  switch (ctrl) {  // the control word must be a constant
+    case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x141, 0xF, 0xF, false));
+    case 0x140: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x140, 0xF, 0xF, false));
+    case 0x142: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x142, 0xA, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), 0x143, 0xC, 0xF, false));
+  }
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32(-INFINITY, v, 0xB1, 0xF));
+  v = fmaxf(v, dpp_f32(-INFINITY, v, 0x4E, 0xF));
+  v = fmaxf(v, dpp_f32(-INFINITY, v, 0x141, 0xF));
+  v = fmaxf(v, dpp_f32(-INFINITY, v, 0x140, 0xF));
+  v = fmaxf(v, dpp_f32(-INFINITY, v, 0x142, 0xA));
+  v = fmaxf(v, dpp_f32(-INFINITY, v, 0x143, 0xC));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32(0.f, v, 0xB1, 0xF);
+  v += dpp_f32(0.f, v, 0x4E, 0xF);
+  v += dpp_f32(0.f, v, 0x141, 0xF);
+  v += dpp_f32(0.f, v, 0x140, 0xF);
+  v += dpp_f32(0.f, v, 0x142, 0xA);
+  v += dpp_f32(0.f, v, 0x143, 0xC);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Inclusive prefix sum over the wave's lanes: shifts by 1, 2, 4 and 8 lanes
 // within each 16-lane row (zero filled), then row broadcasts carry the row
 // totals across rows (lane 15 into row 1 and 3, lane 31 into rows 2 and 3).
