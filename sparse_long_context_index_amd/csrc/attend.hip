@@ -134,6 +134,25 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint3
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
+// Work item of workgroup L of a 1-D grid of N = n_splits * n_hg * T.  The
+// dispatcher deals workgroups to the eight XCDs in turn (L % 8), and each XCD
+// has its own L2; workgroups are numbered so that each XCD takes a run of
+// consecutive items, in which the head groups of one row split (the same
+// rows) are neighbours and share that XCD's L2.
+struct WorkItem {
+  int split, hg, t;
+};
+__device__ __forceinline__ WorkItem work_item(int n_splits, int n_hg) {
+  const int N = (int)gridDim.x, L = (int)blockIdx.x;
+  const int x = L & 7, slot = L >> 3;
+  const int i = x * (N >> 3) + min(x, N & 7) + slot;
+  WorkItem w;
+  w.hg = i % n_hg;
+  w.split = (i / n_hg) % n_splits;
+  w.t = i / (n_hg * n_splits);
+  return w;
+}
+
 // LDS of the tile loop (the fused kernel overlays it on the select's LDS).
 template <int D>
 struct alignas(16) AttSmem {
@@ -146,7 +165,7 @@ struct alignas(16) AttSmem {
 };
 
 // The tile loop and epilogue of one workgroup: rows [row_begin, row_end) of
-// token t for the 16 heads of blockIdx.y.  NT threads stage the tiles; waves
+// token t for the 16 heads of group hg.  NT threads stage the tiles; waves
 // 0-3 run the products and the softmax (the others only join the barriers).
 // Q comes from registers (qa) or from LDS (qlds, 16 rows of D+8); in gather
 // mode the block index of row rr comes from a prefetch of sel_idx (pidx holds
@@ -156,7 +175,8 @@ struct alignas(16) AttSmem {
 // that they are in flight across it.
 template <int D, int MODE, bool HAS_B, int NT, bool Q_LDS, bool SEL_LDS>
 __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& sm, int t,
-                                             int split, int n_splits, int row_begin, int row_end,
+                                             int hg, int split, int n_splits, int row_begin,
+                                             int row_end,
                                              const SegDesc& sd, int32_t pidx,
                                              const int32_t* selrow, bool sel_listed,
                                              const bf16x8 (&qa)[D / 32], const uint16_t* qlds,
@@ -170,7 +190,7 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, quad = lane >> 4;
   const bool mma = NT == 256 || wave < 4;       // waves of the products
-  const int h = blockIdx.y * kHeadsPerWg + li;  // this lane's query head
+  const int h = hg * kHeadsPerWg + li;  // this lane's query head
   uint32_t flags = 0;
   const float sl2 = p.scale * kLog2e;
 
@@ -425,12 +445,12 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   constexpr bool kGather = MODE == kModeGather;
   constexpr int KSQ = D / 32;
   __shared__ AttSmem<D> sm;
-  const int t = blockIdx.z;
-  const int split = blockIdx.x;
+  const WorkItem wi = work_item(n_splits, (p.n_heads + kHeadsPerWg - 1) / kHeadsPerWg);
+  const int t = wi.t, split = wi.split, hg = wi.hg;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int li = lane & 15, quad = lane >> 4;
-  const int h = blockIdx.y * kHeadsPerWg + li;
+  const int h = hg * kHeadsPerWg + li;
 
   // Everything the first tile waits on is loaded up front: its selected block
   // indices (idx rows always hold sel_stride entries), Q, the row metadata.
@@ -452,14 +472,14 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
   const TokMeta meta = load_meta<MODE, HAS_B>(p, t);
   uint32_t flags = 0;
   const SegDesc sd = token_rows<MODE, HAS_B>(p, meta, flags);
-  if (split == 0 && blockIdx.y == 0 && tid == 0) {
+  if (split == 0 && hg == 0 && tid == 0) {
     report(p.err, flags);
     if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
   }
   const int n_rows = sd.alen + sd.blen;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
-  const bool copy_rows = kGather && p.copy_out != nullptr && blockIdx.y == 0;
-  attend_tiles<D, MODE, HAS_B, 256, false, false>(p, sm, t, split, n_splits, row_begin, row_end,
+  const bool copy_rows = kGather && p.copy_out != nullptr && hg == 0;
+  attend_tiles<D, MODE, HAS_B, 256, false, false>(p, sm, t, hg, split, n_splits, row_begin, row_end,
                                                   sd, pidx, nullptr, false, qa, nullptr,
                                                   copy_rows);
 }
@@ -491,8 +511,8 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   __shared__ FusedSmem<D> u;
   __shared__ __attribute__((aligned(16))) uint16_t qlds[kHeadsPerWg * (D + 8)];
   __shared__ int32_t selrow[kFuseMaxTiles * kRT];
-  const int t = blockIdx.z;
-  const int split = blockIdx.x;
+  const WorkItem wi = work_item(n_splits, (p.n_heads + kHeadsPerWg - 1) / kHeadsPerWg);
+  const int t = wi.t, split = wi.split, hg = wi.hg;
   const int tid = threadIdx.x;
   const int row_begin = split * tiles_per_split * kRT;
 
@@ -501,7 +521,7 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   u32x4 qv = u32x4{0u, 0u, 0u, 0u};
   if (tid < kHeadsPerWg * QPR) {
     const int hl = tid / QPR;
-    const int hq = min((int)blockIdx.y * kHeadsPerWg + hl, p.n_heads - 1);
+    const int hq = min(hg * kHeadsPerWg + hl, p.n_heads - 1);
     qv = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)t * p.n_heads + hq) * D +
                                          (tid - hl * QPR) * 8);
   }
@@ -526,7 +546,7 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   meta.a_cnt = (int32_t)r.emitted;
   uint32_t flags = 0;
   const SegDesc sd = token_rows<kModeGather, HAS_B>(p, meta, flags);
-  if (blockIdx.y == 0) {
+  if (hg == 0) {
     // idx entries [row_begin, row_begin + win) below top_k: the selection,
     // then -1
     int32_t* out = sl.idx + (int64_t)t * sl.top_k;
@@ -534,7 +554,7 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
     if ((uint32_t)tid < win && i < (uint32_t)sl.top_k)
       out[i] = i < r.emitted ? (r.listed ? selrow[tid] : (int32_t)i) : -1;
   }
-  if (split == 0 && blockIdx.y == 0) {
+  if (split == 0 && hg == 0) {
     if (tid == 0) {
       sl.count[t] = (int32_t)r.emitted;
       report(p.err, flags | r.flags);
@@ -543,10 +563,10 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   }
   const int n_rows = sd.alen + sd.blen;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
-  const bool copy_rows = p.copy_out != nullptr && blockIdx.y == 0;
+  const bool copy_rows = p.copy_out != nullptr && hg == 0;
   const bf16x8 qa_unused[KSQ] = {};
   attend_tiles<D, kModeGather, HAS_B, kFuseThreads, true, true>(
-      p, u.a, t, split, n_splits, row_begin, row_end, sd, 0, selrow, r.listed, qa_unused, qlds,
+      p, u.a, t, hg, split, n_splits, row_begin, row_end, sd, 0, selrow, r.listed, qa_unused, qlds,
       copy_rows);
 }
 
@@ -664,7 +684,7 @@ template <int D>
 hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
   const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
   const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
-  dim3 grid((unsigned)sp.n_splits, (unsigned)n_hg, (unsigned)a.T);
+  dim3 grid((unsigned)(sp.n_splits * n_hg * a.T));
   const int mode = a.sel_idx != nullptr ? kModeGather
                    : a.vis_pos != nullptr ? kModeVisible
                                           : kModeExplicit;
@@ -698,7 +718,7 @@ template <int D>
 hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStream_t s) {
   const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
   const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
-  dim3 grid((unsigned)sp.n_splits, (unsigned)n_hg, (unsigned)a.T);
+  dim3 grid((unsigned)(sp.n_splits * n_hg * a.T));
   if (a.kv_b != nullptr)
     hipLaunchKernelGGL((select_attend_kernel<D, true>), grid, dim3(kFuseThreads), 0, s, sl, a,
                        sp.tiles_per_split, sp.n_splits);
