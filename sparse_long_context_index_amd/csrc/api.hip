@@ -294,6 +294,7 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
     S.ratio = a->ratio; S.top_k = a->top_k;
     S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
     S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
+    S.slots = select_slots(tp);
     S.idx = idx; S.count = count;
     e = launch_select_attend(S, L, st);
   } else {

@@ -501,7 +501,7 @@ union FusedSmem {
   AttSmem<D> a;
 };
 
-template <int D, bool HAS_B>
+template <int D, bool HAS_B, int KP>
 __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunch sl,
                                                                      AttendLaunch p,
                                                                      int tiles_per_split,
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   }
 
   const uint32_t win = (uint32_t)(tiles_per_split * kRT);  // this split's rows
-  const sel::SelResult r = sel::select_token(
+  const sel::SelResult r = sel::select_token<KP>(
       sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.top_k,
       sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
@@ -719,12 +719,15 @@ hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStre
   const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
   const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
   dim3 grid((unsigned)(sp.n_splits * n_hg * a.T));
-  if (a.kv_b != nullptr)
-    hipLaunchKernelGGL((select_attend_kernel<D, true>), grid, dim3(kFuseThreads), 0, s, sl, a,
-                       sp.tiles_per_split, sp.n_splits);
-  else
-    hipLaunchKernelGGL((select_attend_kernel<D, false>), grid, dim3(kFuseThreads), 0, s, sl, a,
-                       sp.tiles_per_split, sp.n_splits);
+#define CSA_FUSED(HB, KP)                                                                  \
+  hipLaunchKernelGGL((select_attend_kernel<D, HB, KP>), grid, dim3(kFuseThreads), 0, s, sl, a, \
+                     sp.tiles_per_split, sp.n_splits)
+  if (sl.slots == 4) {
+    if (a.kv_b != nullptr) CSA_FUSED(true, 4); else CSA_FUSED(false, 4);
+  } else {
+    if (a.kv_b != nullptr) CSA_FUSED(true, sel::KPT); else CSA_FUSED(false, sel::KPT);
+  }
+#undef CSA_FUSED
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.n_splits == 1) return e;
   hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),

@@ -332,6 +332,7 @@ struct TopkWs {
 };
 TopkWs topk_ws_layout(void* ws, int T, const TopkPlan& p);
 CandArgs cand_args(const TopkPlan& p, const TopkWs& w);
+int select_slots(const TopkPlan& p);  // register key slots per select thread: 4 or 12
 hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* pos,
                               const int32_t* n_comp, int T, int ratio, const TopkPlan& p,
                               const TopkWs& ws, uint32_t* err, hipStream_t s);
@@ -379,6 +380,7 @@ struct SelectLaunch {
   int ratio, top_k;
   const uint64_t* cand; const uint64_t* gcut;
   int list_len, groups_per_token, blocks_per_group;
+  int slots;  // select_slots() of the plan
   int32_t* idx; int32_t* count;
 };
 bool select_attend_fits(int T, int n_heads, int max_rows);

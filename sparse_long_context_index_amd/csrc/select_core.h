@@ -9,7 +9,7 @@
 //
 // The workgroup selects from a key set held in registers (12 keys per
 // thread) plus an LDS overflow area:
-//   * n_vis <= kPoolCap: the keys are every visible block (exact, direct);
+//   * n_vis <= KP * 1024: the keys are every visible block (exact, direct);
 //   * otherwise the keys are the candidate lists of the groups that cover
 //     the row (see CandArgs).  Let T1 be the k_eff-th largest listed key.  A
 //     group whose bound (>= every key it did not list) is >= T1 may hold
@@ -44,7 +44,7 @@ namespace sel {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int KPT = kPoolCap / kThreads;  // register keys per thread
+constexpr int KPT = kPoolCap / kThreads;  // register keys per thread, at most
 constexpr int kBins = 2 * kThreads;       // linear bins, two per thread
 constexpr int kXCap = 4096;               // keys of re-scanned groups (LDS)
 constexpr int kListCap = 1024;            // threshold-bin keys ranked exactly
@@ -236,18 +236,19 @@ __device__ __forceinline__ uint32_t word_bin(uint32_t h, uint32_t ulo, bool smal
   return small ? d : __umulhi(d, mul);
 }
 
-// The k-th largest of the nonzero keys in key[0..KPT) of every thread (slots
+// The k-th largest of the nonzero keys in key[0..KP) of every thread (slots
 // i with i*kThreads >= nk are zero and skipped) and in sh.xk[0..n_x); 0 when
 // fewer than k keys are nonzero.  1 <= k.  Each phase
 // writes its own LDS slots, so six barriers separate the phases (a barrier
 // between a phase's reads and the next call's writes always intervenes).
-__device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t nk, uint32_t n_x,
+template <int KP>
+__device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KP], uint32_t nk, uint32_t n_x,
                                             uint32_t k, SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // ---- count and score-word range of the nonzero keys; clear the histogram ----
   uint32_t nz = 0, ulo = 0xFFFFFFFFu, uhi = 0u;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
+  for (int i = 0; i < KP; ++i) {
     if ((uint32_t)i * kThreads < nk) {
       const bool p = key[i] != 0ull;
       const uint32_t h = (uint32_t)(key[i] >> 32);
@@ -290,7 +291,7 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
   if (!crowded) {
     // ---- histogram of the linear bins ----
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
+    for (int i = 0; i < KP; ++i)
       if ((uint32_t)i * kThreads < nk && key[i] != 0ull)
         atomicAdd(&sh.hist[word_bin((uint32_t)(key[i] >> 32), blo, small, mul)], 1u);
     for (uint32_t j = tid; j < n_x; j += kThreads)
@@ -323,7 +324,7 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
     if (!crowded) {
       // ---- exact rank among the keys of bin b ----
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
+      for (int i = 0; i < KP; ++i)
         if ((uint32_t)i * kThreads < nk)
           wave_append(key[i] != 0ull && word_bin((uint32_t)(key[i] >> 32), blo, small, mul) == b,
                     key[i], sh.list, &sh.n_list, kListCap);
@@ -346,19 +347,19 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KPT], uint32_t
   }
   // ties or tightly clustered scores: exact radix select over all the keys
   auto get = [&](uint32_t j) -> uint64_t {
-    if (j < (uint32_t)kPoolCap) {
+    if (j < (uint32_t)(KP * kThreads)) {
       // register slot of j is (thread j % kThreads, index j / kThreads); only
       // the calling thread's own slots are ever asked for
       const int i = (int)(j / kThreads);
       uint64_t v = 0ull;
 #pragma unroll
-      for (int q = 0; q < KPT; ++q)
+      for (int q = 0; q < KP; ++q)
         if (q == i) v = key[q];
       return v;
     }
-    return sh.xk[j - kPoolCap];
+    return sh.xk[j - KP * kThreads];
   };
-  return radix_kth(get, (uint32_t)kPoolCap + n_x, k, sh);
+  return radix_kth(get, (uint32_t)(KP * kThreads) + n_x, k, sh);
 }
 
 // Marks {block of key : key >= thr, key != 0} of the keys in registers, the
@@ -434,13 +435,14 @@ struct SelResult {
 };
 
 // Top-k of one token over its scores row `srow` (ld entries, n_vis of them
-// visible): every thread of the 1024-thread workgroup calls this with the same
+// visible), holding up to KP keys per thread in registers: every thread of the 1024-thread workgroup calls this with the same
 // arguments.  `cand`/`gcut` are the token's candidate lists and group bounds
 // (list_len keys per group of blocks_per_group blocks, groups_per_token
 // groups; list_len == 0 means none).  On return (after a barrier) the
 // selection is described by the result and, when listed, by dst: the blocks
 // at positions [e_lo, e_hi) of the ascending selection, dst[i] holding
 // position e_lo + i (positions at or past the count are not written).
+template <int KP>
 __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow, int64_t ld,
                                                   int64_t pos_t, int32_t ncomp_t, int ratio,
                                                   int top_k, const uint64_t* __restrict__ cand,
@@ -456,25 +458,25 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
   // so that all of them are in flight together.
   const uint32_t L = list_len > 0 ? (uint32_t)list_len : 1u;
   const uint32_t NG = list_len > 0 ? (uint32_t)groups_per_token : 0u;
-  const uint32_t CT = NG * L;  // <= kPoolCap, and NG <= kMaxGroups (plan_topk)
-  uint64_t key[KPT];
+  const uint32_t CT = NG * L <= (uint32_t)(KP * kThreads) ? NG * L : 0u;  // NG <= kMaxGroups (plan_topk)
+  uint64_t key[KP];
   uint64_t gc[2];
   if (CT > 0u) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
+    for (int i = 0; i < KP; ++i)
       key[i] = (uint32_t)i * kThreads < CT ? cand[min((uint32_t)tid + (uint32_t)i * kThreads, CT - 1u)]
                                            : 0ull;
 #pragma unroll
     for (int i = 0; i < 2; ++i) gc[i] = gcut[min((uint32_t)tid + (uint32_t)i * kThreads, NG - 1u)];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
+    for (int i = 0; i < KP; ++i)
       if ((uint32_t)tid + (uint32_t)i * kThreads >= CT) key[i] = 0ull;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       if ((uint32_t)tid + (uint32_t)i * kThreads >= NG) gc[i] = 0ull;
   } else {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) key[i] = 0ull;
+    for (int i = 0; i < KP; ++i) key[i] = 0ull;
     gc[0] = gc[1] = 0ull;
   }
   // the emission bitmap is cleared while those loads are in flight
@@ -506,21 +508,21 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
     uint32_t n_x = 0;
     uint32_t nk = 0;  // register key slots in use (i*kThreads < nk)
     // a long row without candidate lists selects over its scores in memory
-    bool global_path = n_vis > kPoolCap && CT == 0u;
+    bool global_path = n_vis > KP * kThreads && CT == 0u;
     uint64_t thr = 0ull;
-    if (n_vis <= kPoolCap) {
+    if (n_vis <= KP * kThreads) {
       // ---- direct: every visible block is a key ----
       const uint32_t n = (uint32_t)n_vis;  // >= 1 here
-      float sv[KPT];
+      float sv[KP];
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) sv[i] = srow[min((uint32_t)tid + (uint32_t)i * kThreads, n - 1u)];
+      for (int i = 0; i < KP; ++i) sv[i] = srow[min((uint32_t)tid + (uint32_t)i * kThreads, n - 1u)];
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
+      for (int i = 0; i < KP; ++i) {
         const uint32_t j = (uint32_t)tid + (uint32_t)i * kThreads;
         key[i] = j < n ? block_key(sv[i], j) : 0ull;
       }
       nk = n;
-      thr = kth_key(key, nk, 0, k_eff, sh);
+      thr = kth_key<KP>(key, nk, 0, k_eff, sh);
     } else if (!global_path) {
       // ---- candidate lists of the ng groups that cover the row ----
       const uint32_t G = (uint32_t)blocks_per_group;
@@ -528,9 +530,9 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
       const uint32_t C = min(ng * L, CT);
       nk = C;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
+      for (int i = 0; i < KP; ++i)
         if ((uint32_t)tid + (uint32_t)i * kThreads >= C) key[i] = 0ull;
-      const uint64_t t1 = C >= k_eff ? kth_key(key, nk, 0, k_eff, sh) : 0ull;
+      const uint64_t t1 = C >= k_eff ? kth_key<KP>(key, nk, 0, k_eff, sh) : 0ull;
       // groups that may hold unlisted blocks at or above T1
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -559,7 +561,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
           const uint32_t dq = (uint32_t)kThreads / L, dr = (uint32_t)kThreads - dq * L;
           uint32_t q = (uint32_t)tid / L, r = (uint32_t)tid - q * L;
 #pragma unroll
-          for (int i = 0; i < KPT; ++i) {
+          for (int i = 0; i < KP; ++i) {
             if ((uint32_t)i * kThreads < nk && q < ng && ((sh.gflag[q >> 5] >> (q & 31)) & 1u))
               key[i] = 0ull;
             q += dq;
@@ -592,7 +594,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
           }
           __syncthreads();
           n_x = min(sh.n_x, (uint32_t)kXCap);
-          thr = kth_key(key, nk, n_x, k_eff, sh);
+          thr = kth_key<KP>(key, nk, n_x, k_eff, sh);
           if (thr == 0ull) global_path = true;
         }
       }
@@ -600,7 +602,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
     if (!global_path) {
       auto mark = [&](int64_t base, int64_t len) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i)
+        for (int i = 0; i < KP; ++i)
           if ((uint32_t)i * kThreads < nk && key[i] != 0ull && key[i] >= thr)
             mark_block(key[i], base, len, sh);
         for (uint32_t j = tid; j < n_x; j += kThreads)

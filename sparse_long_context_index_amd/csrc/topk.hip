@@ -11,6 +11,7 @@
 namespace csa {
 namespace {
 
+template <int KP>
 __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
     const int32_t* __restrict__ n_comp, int ratio, int top_k,
@@ -20,7 +21,7 @@ __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
   __shared__ sel::SelShared sh;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  const sel::SelResult r = sel::select_token(
+  const sel::SelResult r = sel::select_token<KP>(
       scores + (int64_t)t * ld, ld, pos[t], n_comp[t], ratio, top_k,
       cand_all + (int64_t)t * groups_per_token * list_len, gcut_all + (int64_t)t * groups_per_token,
       list_len, groups_per_token, blocks_per_group, sh, sh.outl, 0u, (uint32_t)top_k);
@@ -109,6 +110,13 @@ TopkPlan plan_topk(int T, int64_t ld, int top_k) {
   return p;
 }
 
+int select_slots(const TopkPlan& p) {
+  // with candidate lists of at most 4096 keys, four register slots per
+  // thread hold them (and rows of up to 4096 blocks directly); the select's
+  // per-slot work is then a third of the twelve-slot variant's
+  return p.list_len > 0 && (int64_t)p.groups_per_token * p.list_len <= 4096 ? 4 : 12;
+}
+
 CandArgs cand_args(const TopkPlan& p, const TopkWs& w) {
   CandArgs c{};
   c.cand = w.cand;
@@ -148,9 +156,14 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int64_t* po
                               const TopkPlan& p, const TopkWs& ws, int32_t* idx,
                               int32_t* count, uint32_t* err, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)T), dim3(sel::kThreads), 0, s, scores, ld,
-                     pos, n_comp, ratio, top_k, ws.cand, ws.gcut, p.list_len,
-                     p.groups_per_token, p.blocks_per_group, idx, count, err);
+  if (select_slots(p) == 4)
+    hipLaunchKernelGGL((topk_select_kernel<4>), dim3((unsigned)T), dim3(sel::kThreads), 0, s, scores,
+                       ld, pos, n_comp, ratio, top_k, ws.cand, ws.gcut, p.list_len,
+                       p.groups_per_token, p.blocks_per_group, idx, count, err);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<sel::KPT>), dim3((unsigned)T), dim3(sel::kThreads), 0, s,
+                       scores, ld, pos, n_comp, ratio, top_k, ws.cand, ws.gcut, p.list_len,
+                       p.groups_per_token, p.blocks_per_group, idx, count, err);
   return hipGetLastError();
 }
 
