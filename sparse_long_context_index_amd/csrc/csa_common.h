@@ -225,6 +225,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // list holds every block of the group).
 constexpr int kIndexWaves = 8;      // waves per indexer workgroup
 constexpr int kMergeMaxWaveM = 8;   // merged waves' lists fit one wave: kIndexWaves * 8 = 64
+constexpr int kMergedLen = 16;      // keys per merged list
+constexpr int kMergeScratch = 2 * kMergedLen;  // LDS words per wave the merge needs
 struct CandArgs {
   uint64_t* cand; uint64_t* gcut;
   int wave_m;            // keys each wave keeps of its own blocks
@@ -235,12 +237,14 @@ struct CandArgs {
 
 // Publishes a wave's candidate list: lane r < wave_m holds the wave's r-th
 // largest composite key (zero past its valid blocks) and n_ok counts the
-// wave's valid blocks.  Without merging the list is its group's list and the
+// wave's valid blocks.  Lists are stored in ascending block order, zero keys
+// last, so that the select can list its selection in block order from slot
+// positions.  Without merging the list is its group's list and the
 // group bound is the list's last key when the wave has more valid blocks.
 // With merging every wave of the workgroup calls this (it holds a barrier):
 // each wave's list and bound go to LDS (wave w's kMergeMaxWaveM + 1 words at
-// lds + w*lds_stride), and wave 0 keeps the list_len largest of those
-// kIndexWaves*wave_m keys.  A block missing from the merged list is either
+// lds + w*lds_stride, lds_stride >= kMergeScratch), and wave 0 keeps the
+// list_len largest of those kIndexWaves*wave_m keys.  A block missing from the merged list is either
 // below the largest key left out of it, or missing from its wave's list and
 // so below that wave's last key; the bound is the larger of those.
 __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const CandArgs& ca,
@@ -253,7 +257,13 @@ __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const 
   const uint64_t wbound = n_ok > (uint32_t)m ? wlast : 0ull;
   if (!ca.merge) {
     const int64_t g = t * ca.groups_per_token + wave_in_token;
-    if (lane < m) ca.cand[g * ca.list_len + lane] = val;
+    // block order: the nonzero keys are lanes 0..nnz-1
+    const uint32_t blk = ~(uint32_t)val;
+    const int nnz = __popcll(__ballot(lane < m && val != 0ull));
+    uint32_t pos = 0;
+    for (int j = 0; j < nnz; ++j) pos += (uint32_t)__builtin_amdgcn_readlane((int)blk, j) < blk ? 1u : 0u;
+    if (lane >= nnz) pos = (uint32_t)lane;
+    if (lane < m) ca.cand[g * ca.list_len + pos] = val;
     if (lane == 0) ca.gcut[g] = wbound;
     return;
   }
@@ -284,7 +294,21 @@ __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const 
       key != 0ull ? above
                   : nonzero + (uint32_t)__popcll(zero_lanes & ((1ull << lane) - 1ull));
   const int64_t g = t * ca.groups_per_token + wg_in_token;
-  if (rank < (uint32_t)ca.list_len) ca.cand[g * ca.list_len + rank] = key;
+  // the list_len largest keys, in key order, into LDS scratch; then each list
+  // slot takes its block-order position among them
+  uint64_t* tmp = lds + kMergedLen;  // wave 0's region past its own list
+  if (rank < (uint32_t)ca.list_len) tmp[rank] = key;
+  const uint32_t nnz_l = min(nonzero, (uint32_t)ca.list_len);
+  if (lane < ca.list_len) {
+    const uint64_t kl = tmp[lane];
+    const uint32_t bl = ~(uint32_t)kl;
+    uint32_t pos = (uint32_t)lane;
+    if ((uint32_t)lane < nnz_l) {
+      pos = 0;
+      for (uint32_t j = 0; j < nnz_l; ++j) pos += ~(uint32_t)tmp[j] < bl ? 1u : 0u;
+    }
+    ca.cand[g * ca.list_len + pos] = kl;
+  }
   // the largest key left out of the list, and the waves' own bounds
   const uint64_t out_mask = __ballot(rank == (uint32_t)ca.list_len);
   uint64_t cut = out_mask != 0ull ? readlane_u64(key, __ffsll((unsigned long long)out_mask) - 1) : 0ull;

@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   // for the workgroup merge (no DMA into them is pending by then).
   uint64_t* cand_lds = reinterpret_cast<uint64_t*>(&ktile[0][0][0]);
   constexpr int kCandStride = 2 * TILE_CHUNKS * 2;  // u64 words per wave's buffers
+  static_assert(kCandStride >= kMergeScratch, "merge scratch fits a wave's buffers");
   if (!active) {
     if (ca.cand != nullptr)  // empty list and bound (and the merge barrier)
       cand_publish(0ull, 0u, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);

@@ -63,6 +63,7 @@ struct SelShared {
   uint32_t gflag[kMaxGroups / 32];        // the same groups as a bitmap
   int32_t outl[kMaxTopK];                 // the selection, ascending, before the output copy
   uint32_t scratch[2 * kWaves + 8];
+  uint32_t plane[(KPT + 1) / 2 * kWaves]; // per-wave packed slot-plane counts of emit_slots
   uint32_t rc[kWaves];                    // per-wave count / score-word range of kth_key
   uint32_t rlo[kWaves], rhi[kWaves];
   uint32_t fb_w[kWaves];                  // per-wave bin totals of kth_key
@@ -363,7 +364,7 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KP], uint32_t 
 }
 
 // Marks {block of key : key >= thr, key != 0} of the keys in registers, the
-// LDS extras and (if any) the row, in the bitmap (already clear on entry),
+// LDS extras and (if any) the row, in the bitmap,
 // then lists those at positions [e_lo, e_hi) of the ascending block order at
 // dst[0..e_hi-e_lo) (positions below top_k only); returns how
 // many were marked.
@@ -379,10 +380,8 @@ __device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int to
   u32x4* bm4 = reinterpret_cast<u32x4*>(sh.bitmap);
   for (int64_t base = 0; base < n_vis; base += span) {
     const int64_t len = min(span, n_vis - base);
-    if (base > 0) {
-      for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
-      __syncthreads();
-    }
+    for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
     mark(base, len);
     __syncthreads();
     uint32_t wv[WPT];
@@ -421,6 +420,57 @@ __device__ __forceinline__ uint32_t emit_bitmap(Mark mark, int64_t n_vis, int to
     __syncthreads();
   }
   return emitted;
+}
+
+// Emission when the register slots hold keys in ascending block order (slot
+// j = tid + i*kThreads; every visible block in its own slot, or candidate
+// lists stored in block order, group after group) and there are no LDS
+// extras: a selected key's position is the number of selected keys in lower
+// slots.  Each thread packs its slot planes' selected flags two to a word in
+// 16-bit fields (a plane counts at most kThreads), and one workgroup scan of
+// the packed words gives every position.  Writes positions [e_lo, e_hi)
+// below top_k to dst like emit_bitmap; returns the number selected.
+template <int KP>
+__device__ __forceinline__ uint32_t emit_slots(const uint64_t (&key)[KP], uint32_t nk,
+                                               uint64_t thr, int top_k, SelShared& sh,
+                                               int32_t* dst, uint32_t e_lo, uint32_t e_hi) {
+  constexpr int NP = (KP + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (e_hi > (uint32_t)top_k) e_hi = (uint32_t)top_k;
+  bool sel[KP];
+  uint32_t pk[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) pk[p] = 0u;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    sel[i] = (uint32_t)i * kThreads < nk && key[i] != 0ull && key[i] >= thr;
+    pk[i / 2] |= (sel[i] ? 1u : 0u) << (16 * (i & 1));
+  }
+  uint32_t incl[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    incl[p] = wave_incl_scan_u32(pk[p]);
+    if (lane == 63) sh.plane[p * kWaves + wave] = incl[p];
+  }
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t before, after, total;
+    cross_wave_sums(&sh.plane[p * kWaves], before, after, total);
+    const uint32_t excl = before + incl[p] - pk[p];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * p + h;
+      if (i < KP) {
+        const uint32_t o = base + ((excl >> (16 * h)) & 0xFFFFu);
+        if (sel[i] && o >= e_lo && o < e_hi) dst[o - e_lo] = (int32_t)~(uint32_t)key[i];
+        base += (total >> (16 * h)) & 0xFFFFu;
+      }
+    }
+  }
+  __syncthreads();
+  return base;
 }
 
 __device__ __forceinline__ void mark_block(uint64_t c, int64_t base, int64_t len, SelShared& sh) {
@@ -478,11 +528,6 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
 #pragma unroll
     for (int i = 0; i < KP; ++i) key[i] = 0ull;
     gc[0] = gc[1] = 0ull;
-  }
-  // the emission bitmap is cleared while those loads are in flight
-  {
-    u32x4* bm4 = reinterpret_cast<u32x4*>(sh.bitmap);
-    for (int i = tid; i < kBitmapWords / 4; i += kThreads) bm4[i] = u32x4{0u, 0u, 0u, 0u};
   }
   if (tid == 0) {
     sh.n_ov = 0u;
@@ -599,7 +644,9 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
         }
       }
     }
-    if (!global_path) {
+    if (!global_path && n_x == 0u) {
+      res.emitted = emit_slots<KP>(key, nk, thr, top_k, sh, dst, e_lo, e_hi);
+    } else if (!global_path) {
       auto mark = [&](int64_t base, int64_t len) {
 #pragma unroll
         for (int i = 0; i < KP; ++i)

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
     uint32_t* __restrict__ err) {
   constexpr int KPL = 8;  // up to 8 x 32 = 256 blocks per wave
   constexpr int KPH = KPL / 2;
-  constexpr int kStride = kMergeMaxWaveM + 1;
+  constexpr int kStride = kMergeScratch;
   __shared__ uint64_t lds[kIndexWaves * kStride];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -96,7 +96,6 @@ TopkPlan plan_topk(int T, int64_t ld, int top_k) {
   // wave and the token's merged lists still hold at least three times top_k
   // keys.  The select then holds a third as many keys, and a group's expected
   // share of a full row's top-k is at most 16/3 keys, well inside its list.
-  constexpr int kMergedLen = 16;
   if (kIndexWaves * m <= 64 && (int64_t)ip.wgs_per_token * kMergedLen >= 3 * (int64_t)top_k) {
     p.merge = 1;
     p.list_len = kMergedLen;
