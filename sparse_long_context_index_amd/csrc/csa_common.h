@@ -191,7 +191,9 @@ __device__ __forceinline__ int64_t visible_count(int64_t pos, int ratio, int32_t
     *flags |= CSA_DERR_BAD_META;
     return 0;
   }
-  int64_t v = pos / ratio;
+  // 32-bit division when the position fits (a 64-bit one is a long scalar
+  // sequence)
+  int64_t v = pos < (int64_t)0x7FFFFFFF ? (int64_t)((uint32_t)pos / (uint32_t)ratio) : pos / ratio;
   return v < (int64_t)n_comp ? v : (int64_t)n_comp;
 }
 

@@ -229,12 +229,12 @@ __device__ __forceinline__ uint64_t radix_kth(Get get, uint32_t n, uint32_t k, S
 
 // Bin of a score word h >= ulo among kBins bins laid linearly over the
 // ordered-uint32 score words [ulo, ulo + range]: the word difference itself
-// when the range has fewer values than bins, else its product with
-// mul = floor(kBins * 2^32 / (range + 1)), high half.  Non-decreasing in h,
-// and below kBins.
+// when the range has fewer values than bins, else its product with mul
+// (about kBins * 2^32 / (range + 1)), high half, capped at kBins - 1.
+// Non-decreasing in h for any mul, so the bins are ordered.
 __device__ __forceinline__ uint32_t word_bin(uint32_t h, uint32_t ulo, bool small, uint32_t mul) {
   const uint32_t d = h - ulo;
-  return small ? d : __umulhi(d, mul);
+  return small ? d : min(__umulhi(d, mul), (uint32_t)kBins - 1u);
 }
 
 // The k-th largest of the nonzero keys in key[0..KP) of every thread (slots
@@ -287,7 +287,10 @@ __device__ __forceinline__ uint64_t kth_key(const uint64_t (&key)[KP], uint32_t 
   if (n_nz < k) return 0ull;
   const uint32_t range = bhi - blo;
   const bool small = range < (uint32_t)kBins;
-  const uint32_t mul = small ? 0u : (uint32_t)(((uint64_t)kBins << 32) / ((uint64_t)range + 1u));
+  // single-precision reciprocal (a 64-bit division is a long scalar sequence
+  // that every wave would repeat); range >= kBins here, so mul < 2^32
+  const uint32_t mul =
+      small ? 0u : (uint32_t)((float)kBins * 4294967296.0f / ((float)range + 1.0f) * 0.99999f);
   bool crowded = range == 0u;  // one score value: the radix select orders by index
   if (!crowded) {
     // ---- histogram of the linear bins ----
@@ -571,7 +574,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
     } else if (!global_path) {
       // ---- candidate lists of the ng groups that cover the row ----
       const uint32_t G = (uint32_t)blocks_per_group;
-      const uint32_t ng = (uint32_t)((n_vis + G - 1) / G);
+      const uint32_t ng = ((uint32_t)n_vis + G - 1u) / G;  // n_vis < 2^31
       const uint32_t C = min(ng * L, CT);
       nk = C;
 #pragma unroll
