@@ -188,7 +188,8 @@ csa_status csa_topk(const float* scores, int64_t ld, const int64_t* pos, const i
   const TopkWs tw = topk_ws_layout(ws, T, plan);
   hipError_t e = launch_score_cands(scores, ld, pos, n_comp, T, ratio, plan, tw, err, st);
   if (e == hipSuccess)
-    e = launch_topk_select(scores, ld, pos, n_comp, T, ratio, top_k, plan, tw, idx, count, err, st);
+    e = launch_topk_select(scores, ld, pos, n_comp, nullptr, 0, T, ratio, top_k, plan, tw, idx,
+                           count, err, st);
   return hip_status(e);
 }
 
@@ -291,6 +292,7 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   if (select_attend_fits(a->T, a->n_heads, L.max_rows)) {
     SelectLaunch S{};
     S.scores = scores; S.ld = a->max_vis; S.pos = a->pos; S.n_comp = a->n_comp;
+    S.seq_kv = a->seq_kv; S.k_rows = a->k_rows;
     S.ratio = a->ratio; S.top_k = a->top_k;
     S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
     S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
@@ -298,8 +300,8 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
     S.idx = idx; S.count = count;
     e = launch_select_attend(S, L, st);
   } else {
-    e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->T, a->ratio, a->top_k, tp,
-                           tw, idx, count, a->err, st);
+    e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->seq_kv, a->k_rows, a->T,
+                           a->ratio, a->top_k, tp, tw, idx, count, a->err, st);
     if (e == hipSuccess) e = launch_attend(L, st);
   }
   return hip_status(e);

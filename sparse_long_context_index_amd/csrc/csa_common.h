@@ -362,8 +362,10 @@ int select_slots(const TopkPlan& p);  // register key slots per select thread: 4
 hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* pos,
                               const int32_t* n_comp, int T, int ratio, const TopkPlan& p,
                               const TopkWs& ws, uint32_t* err, hipStream_t s);
+// seq_kv == nullptr: caller-given scores with no key buffer to check
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int64_t* pos,
-                              const int32_t* n_comp, int T, int ratio, int top_k,
+                              const int32_t* n_comp, const int64_t* seq_kv, int64_t k_rows,
+                              int T, int ratio, int top_k,
                               const TopkPlan& p, const TopkWs& ws, int32_t* idx,
                               int32_t* count, uint32_t* err, hipStream_t s);
 
@@ -403,6 +405,7 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 // sel_cnt; idx and count are still written.
 struct SelectLaunch {
   const float* scores; int64_t ld; const int64_t* pos; const int32_t* n_comp;
+  const int64_t* seq_kv; int64_t k_rows;  // the indexer's key range check
   int ratio, top_k;
   const uint64_t* cand; const uint64_t* gcut;
   int list_len, groups_per_token, blocks_per_group;

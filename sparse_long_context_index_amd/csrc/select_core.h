@@ -489,7 +489,9 @@ struct SelResult {
 
 // Top-k of one token over its scores row `srow` (ld entries, n_vis of them
 // visible), holding up to KP keys per thread in registers: every thread of the 1024-thread workgroup calls this with the same
-// arguments.  `cand`/`gcut` are the token's candidate lists and group bounds
+// arguments.  A token whose keys would run past the key buffer (key_row0 < 0
+// or key_row0 + n_vis > key_rows) was scored as 0 blocks by the indexer and
+// selects nothing here.  `cand`/`gcut` are the token's candidate lists and group bounds
 // (list_len keys per group of blocks_per_group blocks, groups_per_token
 // groups; list_len == 0 means none).  On return (after a barrier) the
 // selection is described by the result and, when listed, by dst: the blocks
@@ -498,6 +500,7 @@ struct SelResult {
 template <int KP>
 __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow, int64_t ld,
                                                   int64_t pos_t, int32_t ncomp_t, int ratio,
+                                                  int64_t key_row0, int64_t key_rows,
                                                   int top_k, const uint64_t* __restrict__ cand,
                                                   const uint64_t* __restrict__ gcut, int list_len,
                                                   int groups_per_token, int blocks_per_group,
@@ -539,6 +542,7 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
   if (tid < kMaxGroups / 32) sh.gflag[tid] = 0u;
   uint32_t f = 0;
   int64_t n_vis = visible_count(pos_t, ratio, ncomp_t, &f);
+  if (key_row0 < 0 || key_row0 + n_vis > key_rows) n_vis = 0;  // flagged by the indexer
   if (n_vis > ld) {
     f |= CSA_DERR_VIS_OVER_LD;
     n_vis = ld;

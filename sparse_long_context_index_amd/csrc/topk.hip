@@ -14,16 +14,16 @@ namespace {
 template <int KP>
 __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ pos,
-    const int32_t* __restrict__ n_comp, int ratio, int top_k,
-    const uint64_t* __restrict__ cand_all, const uint64_t* __restrict__ gcut_all, int list_len,
+    const int32_t* __restrict__ n_comp, const int64_t* __restrict__ seq_kv, int64_t k_rows,
+    int ratio, int top_k, const uint64_t* __restrict__ cand_all, const uint64_t* __restrict__ gcut_all, int list_len,
     int groups_per_token, int blocks_per_group, int32_t* __restrict__ idx,
     int32_t* __restrict__ count, uint32_t* __restrict__ err) {
   __shared__ sel::SelShared sh;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
   const sel::SelResult r = sel::select_token<KP>(
-      scores + (int64_t)t * ld, ld, pos[t], n_comp[t], ratio, top_k,
-      cand_all + (int64_t)t * groups_per_token * list_len, gcut_all + (int64_t)t * groups_per_token,
+      scores + (int64_t)t * ld, ld, pos[t], n_comp[t], ratio,
+      seq_kv != nullptr ? seq_kv[t] : 0, seq_kv != nullptr ? k_rows : INT64_MAX, top_k, cand_all + (int64_t)t * groups_per_token * list_len, gcut_all + (int64_t)t * groups_per_token,
       list_len, groups_per_token, blocks_per_group, sh, sh.outl, 0u, (uint32_t)top_k);
   // one coalesced pass writes the selection and the -1 padding
   int32_t* out = idx + (int64_t)t * top_k;
@@ -151,17 +151,18 @@ hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* po
 }
 
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int64_t* pos,
-                              const int32_t* n_comp, int T, int ratio, int top_k,
+                              const int32_t* n_comp, const int64_t* seq_kv, int64_t k_rows,
+                              int T, int ratio, int top_k,
                               const TopkPlan& p, const TopkWs& ws, int32_t* idx,
                               int32_t* count, uint32_t* err, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (select_slots(p) == 4)
     hipLaunchKernelGGL((topk_select_kernel<4>), dim3((unsigned)T), dim3(sel::kThreads), 0, s, scores,
-                       ld, pos, n_comp, ratio, top_k, ws.cand, ws.gcut, p.list_len,
+                       ld, pos, n_comp, seq_kv, k_rows, ratio, top_k, ws.cand, ws.gcut, p.list_len,
                        p.groups_per_token, p.blocks_per_group, idx, count, err);
   else
     hipLaunchKernelGGL((topk_select_kernel<sel::KPT>), dim3((unsigned)T), dim3(sel::kThreads), 0, s,
-                       scores, ld, pos, n_comp, ratio, top_k, ws.cand, ws.gcut, p.list_len,
+                       scores, ld, pos, n_comp, seq_kv, k_rows, ratio, top_k, ws.cand, ws.gcut, p.list_len,
                        p.groups_per_token, p.blocks_per_group, idx, count, err);
   return hipGetLastError();
 }

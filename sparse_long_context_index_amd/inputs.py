@@ -166,6 +166,28 @@ def synth(
     )
 
 
+def plant_keys(inp: CSAInputs, t: int, blocks: Sequence[int], seed: int,
+               jitter: float = 0.05) -> np.ndarray:
+    """Overwrite the indexer keys of token t's visible blocks ``blocks`` with
+    keys aligned to that token's query direction v = sum_h w_h q_idx[t,h]
+    (norm sqrt(ihd), the norm of a typical N(0,1) key) plus independent
+    N(0, jitter^2) noise per component, so that the planted blocks stand out
+    from the random ones while their own values stay distinct.  Modifies
+    ``inp.k_idx`` in place and returns the sorted planted block indices."""
+    blocks = np.unique(np.asarray(blocks, dtype=np.int64))
+    n_vis = int(min(inp.pos[t] // inp.ratio, inp.n_comp[t]))
+    if blocks.size and (blocks.min() < 0 or blocks.max() >= n_vis):
+        raise ValueError("planted blocks must be visible to the token")
+    qf = bf16_bits_to_f32(inp.q_idx[t]).astype(np.float64)
+    v = (inp.w[t].astype(np.float64)[:, None] * qf).sum(axis=0)
+    key = np.sqrt(inp.ihd) * v / np.linalg.norm(v)
+    rng = np.random.default_rng(seed)
+    noise = rng.standard_normal((blocks.size, inp.ihd), dtype=np.float32) * np.float32(jitter)
+    rows = (key.astype(np.float32)[None, :] + noise).astype(np.float32)
+    inp.k_idx[int(inp.seq_kv[t]) + blocks] = f32_to_bf16_bits(rows)
+    return blocks
+
+
 @dataclass
 class HCAInputs:
     """Dense heavily-compressed-attention inputs (ratio 128, no indexer)."""

@@ -85,3 +85,26 @@ def check_attention(out_bf16_as_f32, q_bits, rows_bits, scale, sink=None, what="
         if fin.any():
             assert np.abs(lse[fin] - ref_lse[fin]).max() <= 1e-3 * np.maximum(1, np.abs(ref_lse[fin])).max()
     return float(err), float(cos.min())
+
+
+def check_step(inp, res, tokens=None, sink=None):
+    """Scores, top-k, the gathered all_kv rows (bit-exact) and attention of
+    the given tokens of one decode-step result against the oracle; returns the
+    mean top-k recall."""
+    tokens = range(inp.T) if tokens is None else tokens
+    assert res["err"] == 0, f"device error {res['err']:#x}"
+    recalls = []
+    for t in tokens:
+        n, I, A = ref_scores(inp, t)
+        check_scores(res["scores"][t, :n], I, A, f"scores t={t}")
+        cnt = int(res["count"][t])
+        recalls.append(check_topk(res["idx"][t], cnt, I, A, inp.top_k, f"top-k t={t}"))
+        sel = res["idx"][t, :cnt]
+        # gather: bit-exact against the GPU's own selection
+        s0, sl = int(inp.swa_row0[t]), int(inp.swa_len[t])
+        rows = np.concatenate([inp.comp_kv[int(inp.seq_kv[t]) + sel], inp.swa[s0:s0 + sl]])
+        assert int(res["n_kv"][t]) == len(rows)
+        assert np.array_equal(res["all_kv"][t, :len(rows)], rows), f"gather t={t}"
+        check_attention(res["out"][t], inp.q[t], rows, inp.scale, sink, what=f"attend t={t}",
+                        lse=res["lse"][t])
+    return float(np.mean(recalls)) if recalls else 1.0

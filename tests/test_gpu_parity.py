@@ -13,7 +13,8 @@ import torch
 from oracle import (bf16_to_f64, csa_token, hca_token, select_top_blocks,
                     shared_kv_attention, visible_blocks)
 from sparse_long_context_index_amd import inputs as gen
-from tests._parity import (check_attention, check_scores, check_topk, ref_scores, say)
+from tests._parity import (check_attention, check_scores, check_step, check_topk, ref_scores,
+                           say)
 
 pytestmark = pytest.mark.gpu
 
@@ -265,31 +266,11 @@ def test_mqa_attend(dev, head_dim, n_heads, lens, two, sink):
 # S5: whole decode step
 # ---------------------------------------------------------------------------
 
-def _check_step(inp, res, tokens=None, sink=None):
-    tokens = range(inp.T) if tokens is None else tokens
-    assert res["err"] == 0, f"device error {res['err']:#x}"
-    recalls = []
-    for t in tokens:
-        n, I, A = ref_scores(inp, t)
-        check_scores(res["scores"][t, :n], I, A, f"scores t={t}")
-        cnt = int(res["count"][t])
-        recalls.append(check_topk(res["idx"][t], cnt, I, A, inp.top_k, f"top-k t={t}"))
-        sel = res["idx"][t, :cnt]
-        # gather: bit-exact against the GPU's own selection
-        s0, sl = int(inp.swa_row0[t]), int(inp.swa_len[t])
-        rows = np.concatenate([inp.comp_kv[int(inp.seq_kv[t]) + sel], inp.swa[s0:s0 + sl]])
-        assert int(res["n_kv"][t]) == len(rows)
-        assert np.array_equal(res["all_kv"][t, :len(rows)], rows), f"gather t={t}"
-        check_attention(res["out"][t], inp.q[t], rows, inp.scale, sink, what=f"attend t={t}",
-                        lse=res["lse"][t])
-    return float(np.mean(recalls)) if recalls else 1.0
-
-
 def test_decode_step_tiny(dev):
     say("csa_decode_step tiny (pos 255, 63 blocks, top_k 16)")
     inp = gen.tiny()
     res = B().run_decode_step(inp, dev)
-    _check_step(inp, res)
+    check_step(inp, res)
     ref = csa_token(inp, 0)
     assert sorted(res["idx"][0, :16].tolist()) == sorted(ref["sel"].tolist())
 
@@ -301,7 +282,7 @@ def test_decode_step_ragged_batch(dev):
                     n_comp_seq=[n + 1 for n in lens], n_ih=64, ihd=128, ratio=4, top_k=128,
                     window=32, n_heads=16, head_dim=128, w_std=0.125)
     res = B().run_decode_step(inp, dev)
-    _check_step(inp, res)
+    check_step(inp, res)
     assert res["count"].tolist() == [0, 3, 128, 128, 77]
 
 
@@ -311,14 +292,14 @@ def test_decode_step_sink(dev):
                     window=16, n_heads=8, head_dim=256, w_std=0.35)
     sink = np.linspace(-2, 3, 8).astype(np.float32)
     res = B().run_decode_step(inp, dev, sink=torch.from_numpy(sink).to(dev))
-    _check_step(inp, res, sink=sink)
+    check_step(inp, res, sink=sink)
 
 
 def test_decode_step_32k_planted(dev):
     say("csa_decode_step 32K context, 16 planted blocks")
     inp = gen.ctx32k()
     res = B().run_decode_step(inp, dev)
-    _check_step(inp, res)
+    check_step(inp, res)
     assert set(inp.planted.tolist()) <= set(res["idx"][0, :1024].tolist())
 
 
@@ -326,7 +307,7 @@ def test_decode_step_1m(dev):
     say("csa_decode_step 1M context (262,144 blocks, top_k 1024, 64x512 attention)")
     inp = gen.ctx1m()
     res = B().run_decode_step(inp, dev)
-    recall = _check_step(inp, res)
+    recall = check_step(inp, res)
     say(f"  recall vs fp64 oracle: {recall:.5f}")
     assert recall >= 0.997
 
@@ -344,7 +325,7 @@ def test_decode_step_batched(dev):
     say("csa_decode_step batched: 32 sequences of 16K..128K tokens")
     inp = gen.batched()
     res = B().run_decode_step(inp, dev)
-    _check_step(inp, res)
+    check_step(inp, res)
 
 
 @pytest.mark.parametrize("n_seq", [4, 8])
@@ -356,14 +337,14 @@ def test_decode_step_small_batch_multitile(dev, n_seq):
     say(f"csa_decode_step small batch: {n_seq} sequences of 64K..80K tokens")
     inp = gen.batched(5, n_seq=n_seq, lo=65536, hi=81920)
     res = B().run_decode_step(inp, dev)
-    _check_step(inp, res)
+    check_step(inp, res)
 
 
 def test_decode_step_prefill_sampled(dev):
     say("csa_decode_step prefill chunk: 4096 tokens at 61,440..65,535 (sampled check)")
     inp = gen.prefill()
     res = B().run_decode_step(inp, dev)
-    _check_step(inp, res, tokens=[0, 1, 2047, 3000, 4094, 4095])
+    check_step(inp, res, tokens=[0, 1, 2047, 3000, 4094, 4095])
     # every token: count and causality
     nv = np.minimum(inp.pos // 4, inp.n_comp)
     assert (res["count"] == np.minimum(1024, nv)).all()
