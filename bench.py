@@ -107,9 +107,9 @@ def main() -> int:
         dl["k_idx"] = d0["k_idx"].clone()
         dl["comp_kv"] = d0["comp_kv"].clone()
         layers.append(dl)
-    outs = B.alloc_step_outputs(inp, dev, keep=False)
+    outs = B.alloc_step_outputs(inp, dev, keep=False, all_kv=False)
     step_args = [B.step_args(inp, dl, outs) for dl in layers]
-    ws = torch.empty(B.csa_decode_step_workspace_bytes(step_args[0]), dtype=torch.uint8, device=dev)
+    ws = B.step_workspace(step_args[0], dev)
     torch.cuda.synchronize()
     print("bench: warmup", file=sys.stderr, flush=True)
 

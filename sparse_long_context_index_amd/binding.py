@@ -179,6 +179,13 @@ def csa_decode_step_workspace_bytes(args: StepArgs) -> int:
     return int(load().csa_decode_step_workspace_bytes(ctypes.byref(args)))
 
 
+def step_workspace(args: StepArgs, dev) -> "torch.Tensor":
+    """A decode-step workspace of the size the C ABI asks for (its contents
+    on entry do not matter; it is zero-filled here only for reproducibility)."""
+    import torch
+    return torch.zeros(max(csa_decode_step_workspace_bytes(args), 1), dtype=torch.uint8, device=dev)
+
+
 def csa_decode_step(args: StepArgs, ws, stream=None):
     _check("csa_decode_step", load().csa_decode_step(
         ctypes.byref(args), _p(ws, (torch.uint8,), "ws", True), 0 if ws is None else ws.numel(),
@@ -230,15 +237,18 @@ def step_args(inp, d: dict, outs: dict, mode: int = CSA_MODE_CSA, max_vis: Optio
     return a
 
 
-def alloc_step_outputs(inp, dev, max_vis: Optional[int] = None, keep=True) -> dict:
+def alloc_step_outputs(inp, dev, max_vis: Optional[int] = None, keep=True,
+                       all_kv=True) -> dict:
     mv = int(max_vis if max_vis is not None else max(inp.max_visible(), 1))
     T = inp.T
     o = {
-        "all_kv": torch.zeros((T, inp.top_k + inp.window, inp.head_dim), dtype=torch.bfloat16, device=dev),
         "out": torch.zeros((T, inp.n_heads, inp.head_dim), dtype=torch.bfloat16, device=dev),
         "lse": torch.zeros((T, inp.n_heads), dtype=torch.float32, device=dev),
         "err": torch.zeros(1, dtype=torch.int32, device=dev),
     }
+    if all_kv:
+        o["all_kv"] = torch.zeros((T, inp.top_k + inp.window, inp.head_dim), dtype=torch.bfloat16,
+                                  device=dev)
     if keep:
         o["scores"] = torch.zeros((T, mv), dtype=torch.float32, device=dev)
         o["idx"] = torch.zeros((T, inp.top_k), dtype=torch.int32, device=dev)
@@ -247,12 +257,12 @@ def alloc_step_outputs(inp, dev, max_vis: Optional[int] = None, keep=True) -> di
     return o
 
 
-def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None) -> dict:
+def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None, all_kv: bool = True) -> dict:
     """Upload a batch, run one csa_decode_step, return host copies."""
     d = upload(inp, dev)
-    outs = alloc_step_outputs(inp, dev)
+    outs = alloc_step_outputs(inp, dev, all_kv=all_kv)
     a = step_args(inp, d, outs, sink=sink)
-    ws = torch.empty(max(csa_decode_step_workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
+    ws = step_workspace(a, dev)
     csa_decode_step(a, ws)
     torch.cuda.synchronize(dev)
     res = {k: v.cpu() for k, v in outs.items()}
@@ -260,6 +270,7 @@ def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None) -> dict:
         "scores": res["scores"].numpy(), "idx": res["idx"].numpy(), "count": res["count"].numpy(),
         "n_kv": res["n_kv"].numpy(), "lse": res["lse"].numpy(), "err": int(res["err"][0]),
         "out": res["out"].float().numpy(),
-        "all_kv": res["all_kv"].view(torch.int16).numpy().view(np.uint16),
     }
+    if all_kv:
+        r["all_kv"] = res["all_kv"].view(torch.int16).numpy().view(np.uint16)
     return r

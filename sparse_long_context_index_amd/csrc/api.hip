@@ -91,7 +91,7 @@ StepWs step_ws_layout(const csa_step_args* a) {
     w.scores = off;
     if (!a->scores) off += align256((size_t)a->T * (size_t)a->max_vis * 4);
     w.topk = off;
-    off += topk_ws_layout(nullptr, a->T, plan_topk(a->T, a->max_vis, a->top_k)).bytes;
+    off += topk_ws_layout(nullptr, a->T, plan_topk(a->T, a->max_vis, a->top_k, kStepPool)).bytes;
     w.idx = off;
     if (!a->idx) off += align256((size_t)a->T * a->top_k * 4);
     w.count = off;
@@ -99,11 +99,11 @@ StepWs step_ws_layout(const csa_step_args* a) {
     w.n_kv = off;
     if (!a->n_kv) off += align256((size_t)a->T * 4);
     w.attend = off;
-    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, a->top_k + a->window);
+    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, a->top_k + a->window, kStepSplitTiles);
   } else {
     w.attend = off;
     const int64_t rows = a->max_vis + a->window;
-    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, rows > INT32_MAX ? INT32_MAX : (int)rows);
+    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, rows > INT32_MAX ? INT32_MAX : (int)rows, 0);
   }
   w.total = off;
   return w;
@@ -125,9 +125,10 @@ csa_status check_step(const csa_step_args* a) {
     return CSA_EUNSUPPORTED;
   if (a->max_vis + a->window > INT32_MAX) return CSA_EUNSUPPORTED;
   if (a->mode == CSA_MODE_CSA) {
-    if (!a->q_idx || !a->w || !a->k_idx || !a->all_kv) return CSA_EINVAL;
+    if (!a->q_idx || !a->w || !a->k_idx) return CSA_EINVAL;
     if (a->n_ih < 1 || a->top_k < 1 || a->max_vis < 1 || a->k_rows < 0) return CSA_EINVAL;
-    if (!aligned16(a->q_idx) || !aligned16(a->k_idx) || !aligned16(a->all_kv) || !aligned4(a->w))
+    if (!aligned16(a->q_idx) || !aligned16(a->k_idx) || (a->all_kv && !aligned16(a->all_kv)) ||
+        !aligned4(a->w))
       return CSA_EINVAL;
     if ((a->scores && !aligned16(a->scores)) || (a->idx && !aligned4(a->idx)) ||
         (a->count && !aligned4(a->count)) || (a->n_kv && !aligned4(a->n_kv)))
@@ -173,7 +174,7 @@ csa_status csa_index_score(const uint16_t* q_idx, const float* w, const uint16_t
 
 size_t csa_topk_workspace_bytes(int T, int64_t ld, int top_k) {
   if (T <= 0 || ld <= 0 || ld > INT32_MAX || top_k < 1) return 0;
-  return topk_ws_layout(nullptr, T, plan_topk(T, ld, top_k)).bytes;
+  return topk_ws_layout(nullptr, T, plan_topk(T, ld, top_k, kPoolCap)).bytes;
 }
 
 csa_status csa_topk(const float* scores, int64_t ld, const int64_t* pos, const int32_t* n_comp,
@@ -181,7 +182,7 @@ csa_status csa_topk(const float* scores, int64_t ld, const int64_t* pos, const i
                     size_t ws_bytes, uint32_t* err, void* stream) {
   csa_status s = check_topk(scores, ld, pos, n_comp, T, ratio, top_k, idx, count);
   if (s != CSA_OK || T == 0) return s;
-  const TopkPlan plan = plan_topk(T, ld, top_k);
+  const TopkPlan plan = plan_topk(T, ld, top_k, kPoolCap);
   s = check_ws(ws, ws_bytes, topk_ws_layout(nullptr, T, plan).bytes);
   if (s != CSA_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -212,7 +213,7 @@ csa_status csa_gather(const uint16_t* comp_kv, int64_t comp_rows, const int64_t*
 
 size_t csa_attend_workspace_bytes(int T, int n_heads, int head_dim, int max_rows) {
   if (T <= 0 || n_heads <= 0 || !head_dim_ok(head_dim) || max_rows < 0) return 0;
-  return attend_ws_bytes(T, n_heads, head_dim, max_rows);
+  return attend_ws_bytes(T, n_heads, head_dim, max_rows, 0);
 }
 
 csa_status csa_mqa_attend(const uint16_t* q, int T, int n_heads, int head_dim, float scale,
@@ -226,14 +227,14 @@ csa_status csa_mqa_attend(const uint16_t* q, int T, int n_heads, int head_dim, f
   if (s != CSA_OK) return s;
   if (!a_row0 || !a_len) return CSA_EINVAL;
   if (T == 0) return CSA_OK;
-  s = check_ws(ws, ws_bytes, attend_ws_bytes(T, n_heads, head_dim, max_rows));
+  s = check_ws(ws, ws_bytes, attend_ws_bytes(T, n_heads, head_dim, max_rows, 0));
   if (s != CSA_OK) return s;
   AttendLaunch L{};
   L.q = q; L.T = T; L.n_heads = n_heads; L.head_dim = head_dim; L.scale = scale; L.sink = sink;
   L.kv_a = kv_a; L.a_rows = a_rows; L.a_row0 = a_row0; L.a_len = a_len; L.a_stride = 0;
   L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
   L.kv_b = kv_b; L.b_rows = b_rows; L.b_row0 = b_row0; L.b_len = b_len;
-  L.max_rows = max_rows; L.out = out; L.lse = lse; L.ws = ws; L.err = err;
+  L.max_rows = max_rows; L.split_tiles = 0; L.out = out; L.lse = lse; L.ws = ws; L.err = err;
   return hip_status(launch_attend(L, static_cast<hipStream_t>(stream)));
 }
 
@@ -262,6 +263,7 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
     L.a_stride = 0; L.vis_pos = a->pos; L.vis_ncomp = a->n_comp; L.vis_ratio = a->ratio;
     L.kv_b = a->swa; L.b_rows = a->swa_rows; L.b_row0 = a->swa_row0; L.b_len = a->swa_len;
     L.max_rows = (int)(a->max_vis + a->window);
+    L.split_tiles = 0;
     return hip_status(launch_attend(L, st));
   }
 
@@ -269,11 +271,10 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   int32_t* idx = a->idx ? a->idx : reinterpret_cast<int32_t*>(base + lay.idx);
   int32_t* count = a->count ? a->count : reinterpret_cast<int32_t*>(base + lay.count);
   int32_t* n_kv = a->n_kv ? a->n_kv : reinterpret_cast<int32_t*>(base + lay.n_kv);
-  const TopkPlan tp = plan_topk(a->T, a->max_vis, a->top_k);
+  const TopkPlan tp = plan_topk(a->T, a->max_vis, a->top_k, kStepPool);
   const TopkWs tw = topk_ws_layout(base + lay.topk, a->T, tp);
 
-  // S1 (+ per-wave candidate lists), then S2 with S3 fused into S4: one
-  // select-and-attend kernel for small batches, else top-k then attention.
+  // S1 with its candidate lists
   IndexScoreLaunch I{};
   I.q_idx = a->q_idx; I.w = a->w; I.k_idx = a->k_idx; I.k_rows = a->k_rows;
   I.pos = a->pos; I.seq_kv = a->seq_kv; I.n_comp = a->n_comp;
@@ -282,6 +283,9 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   I.cand = cand_args(tp, tw); I.err = a->err;
   hipError_t e = launch_index_score(I, st);
   if (e != hipSuccess) return hip_status(e);
+  // S2, then S3 fused into S4: the selected compressed rows are read through
+  // their block indices and the SWA rows in place (and copied into all_kv
+  // when it is given)
   L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
   L.a_stride = 0; L.vis_pos = nullptr; L.vis_ncomp = nullptr; L.vis_ratio = 1;
   L.sel_idx = idx; L.sel_cnt = count; L.sel_stride = a->top_k;
@@ -289,21 +293,18 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   L.b_cap = a->window;
   L.copy_out = a->all_kv; L.copy_stride = a->top_k + a->window; L.n_kv_out = n_kv;
   L.max_rows = a->top_k + a->window;
-  if (select_attend_fits(a->T, a->n_heads, L.max_rows)) {
-    SelectLaunch S{};
-    S.scores = scores; S.ld = a->max_vis; S.pos = a->pos; S.n_comp = a->n_comp;
-    S.seq_kv = a->seq_kv; S.k_rows = a->k_rows;
-    S.ratio = a->ratio; S.top_k = a->top_k;
-    S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
-    S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
-    S.slots = select_slots(tp);
-    S.idx = idx; S.count = count;
-    e = launch_select_attend(S, L, st);
-  } else {
-    e = launch_topk_select(scores, a->max_vis, a->pos, a->n_comp, a->seq_kv, a->k_rows, a->T,
-                           a->ratio, a->top_k, tp, tw, idx, count, a->err, st);
-    if (e == hipSuccess) e = launch_attend(L, st);
-  }
+  L.split_tiles = kStepSplitTiles;
+  SelectLaunch S{};
+  S.scores = scores; S.ld = a->max_vis; S.pos = a->pos; S.n_comp = a->n_comp;
+  S.seq_kv = a->seq_kv; S.k_rows = a->k_rows;
+  S.ratio = a->ratio; S.top_k = a->top_k;
+  S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
+  S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
+  S.idx = idx; S.count = count; S.err = a->err;
+  if (select_attend_fits(a->T, a->n_heads, L.max_rows, L.split_tiles))
+    return hip_status(launch_select_attend(S, L, st));
+  e = launch_step_select(S, a->T, st);
+  if (e == hipSuccess) e = launch_attend(L, st);
   return hip_status(e);
 }
 

@@ -153,7 +153,14 @@ __device__ __forceinline__ WorkItem work_item(int n_splits, int n_hg) {
   return w;
 }
 
-// LDS of the tile loop (the fused kernel overlays it on the select's LDS).
+// Split partials in the workspace: (max, sum) fp32 pairs per (token, split,
+// head), then the bf16 outputs, 256-byte aligned.
+__host__ __device__ inline size_t part_ml_floats(int T, int n_splits, int n_heads) {
+  const size_t n = (size_t)T * n_splits * n_heads * 2;
+  return (n + 63) & ~(size_t)63;
+}
+
+// LDS of the tile loop.
 template <int D>
 struct alignas(16) AttSmem {
   using L = Layout<D>;
@@ -242,7 +249,13 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
       // all_kv. ----
       constexpr int NB = (kRT / 8) * DP;     // 8x8 blocks per tile
       constexpr int BPTH = (NB + NT - 1) / NT;  // blocks per thread
+      // Every load is issued unconditionally (a load under a branch per row
+      // keeps the loads from overlapping: measured 2.6x slower for a 64-row
+      // tile): a missing row reads this token's own query row instead, an
+      // address always in bounds, and is zeroed once it has arrived.
+      const uint16_t* safe = p.q + (int64_t)t * p.n_heads * D;
       u32x4 rows[BPTH][8];
+      bool have[BPTH][8];
   #pragma unroll
       for (int q = 0; q < BPTH; ++q) {
         const int b = tid + q * NT;
@@ -252,28 +265,29 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
           const int row = 32 * (g >> 2) + 16 * (k >> 2) + 4 * (g & 3) + (k & 3);
           int64_t src = -1;
           if constexpr (direct) {
-            const int rr = r0 + row;
-            if (b < NB && rr < row_end) {
-              if (rr < sd.alen) {
-                const int64_t ar = sd.a0 + (sel_listed ? selrow[rr - row_begin] : rr);
-                if (ar < 0 || ar >= p.a_rows)
-                  flags |= CSA_DERR_ROW_RANGE;
-                else
-                  src = ar * D;
-              } else {
-                src = ((sd.b0 + (rr - sd.alen)) * D) | kSegB;
-              }
-            }
-          } else if (b < NB) {
-            src = sm.rsrc[row];
+            const int rr = r0 + row;  // the first tile of the split: r0 == row_begin
+            const int32_t sidx = selrow[row];
+            const int64_t ar = sd.a0 + (sel_listed ? sidx : rr);
+            const bool in_a = rr < sd.alen;
+            const bool ok_a = ar >= 0 && ar < p.a_rows;
+            if (b < NB && rr < row_end && in_a && !ok_a) flags |= CSA_DERR_ROW_RANGE;
+            src = (b < NB && rr < row_end)
+                      ? (in_a ? (ok_a ? ar * D : -1) : (((sd.b0 + (rr - sd.alen)) * D) | kSegB))
+                      : -1;
+          } else {
+            src = b < NB ? sm.rsrc[row] : -1;
           }
-          rows[q][k] = u32x4{0u, 0u, 0u, 0u};
-          if (src >= 0) {
-            const uint16_t* base = (src & kSegB) ? kv_b : kv_a;
-            rows[q][k] = *reinterpret_cast<const u32x4*>(base + (src & ~kSegB) + dp * 8);
-          }
+          have[q][k] = src >= 0;
+          const uint16_t* base = (src & kSegB) ? kv_b : kv_a;
+          const uint16_t* a = src >= 0 ? base + (src & ~kSegB) + dp * 8 : safe + (dp & (DP - 1)) * 8;
+          rows[q][k] = *reinterpret_cast<const u32x4*>(a);
         }
       }
+  #pragma unroll
+      for (int q = 0; q < BPTH; ++q)
+  #pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (!have[q][k]) rows[q][k] = u32x4{0u, 0u, 0u, 0u};
       if constexpr (direct) __syncthreads();  // the select's LDS (aliased by sm) is free from here
   #pragma unroll
       for (int q = 0; q < BPTH; ++q) {
@@ -426,12 +440,19 @@ __device__ __forceinline__ void attend_tiles(const AttendLaunch& p, AttSmem<D>& 
     if (p.lse != nullptr && wave == 0 && quad == 0)
       p.lse[(int64_t)t * p.n_heads + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
   } else {
-    float* part_o = static_cast<float*>(p.ws);
-    float* part_ml = part_o + (size_t)p.T * n_splits * p.n_heads * D;
+    // split partial: the split's own softmax output (normalised by its sum)
+    // in bf16, and its (max, sum) in fp32
+    float* part_ml = static_cast<float*>(p.ws);
+    uint16_t* part_o = reinterpret_cast<uint16_t*>(part_ml + part_ml_floats(p.T, n_splits, p.n_heads));
     const size_t slot = ((size_t)t * n_splits + split) * p.n_heads + h;
-    float* po = part_o + slot * D + 4 * quad;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* po = part_o + slot * D + 4 * quad;
 #pragma unroll
-    for (int nn = 0; nn < NTW; ++nn) *reinterpret_cast<f32x4*>(po + (wave * NTW + nn) * 16) = o[nn];
+    for (int nn = 0; nn < NTW; ++nn) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(o[nn][0] * inv) | ((uint32_t)f32_to_bf16(o[nn][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(o[nn][2] * inv) | ((uint32_t)f32_to_bf16(o[nn][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(po + (wave * NTW + nn) * 16) = make_uint2(lo, hi);
+    }
     if (wave == 0 && quad == 0) {
       part_ml[slot * 2 + 0] = m_run;
       part_ml[slot * 2 + 1] = l_run;
@@ -484,24 +505,73 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendLaunch p, int t
                                                   copy_rows);
 }
 
-// Select and attend in one kernel (decode step, CSA).  Every workgroup of
-// token t -- one per (row split, 16-head group) -- first runs the token's
-// exact top-k (the 1024-thread select of select_core.h, repeated by each
-// workgroup so that no kernel boundary or global handoff separates the two
-// stages), which lists the selected block indices of its own rows in LDS, and
-// runs the tile loop over them and the SWA rows.  The select's LDS is reused
-// for the tiles.  The head-group-0 workgroups write the idx entries of their
-// rows; split 0 writes the count.
+// Gather-mode attention of the decode step (CSA rows: the selected
+// compressed rows through their block indices, then the SWA rows in place).
+// A 1024-thread workgroup per (row split, 16-head group, token): the split's
+// block indices, the queries (to LDS) and the row metadata are loaded
+// together, then 512 threads fetch each 64-row tile with eight 16-byte loads
+// apiece, all in flight at once.
+template <int D, bool HAS_B>
+__global__ __launch_bounds__(1024) void gather_attend_kernel(AttendLaunch p, int tiles_per_split,
+                                                             int n_splits) {
+  constexpr int KSQ = D / 32;
+  constexpr int QPR = D / 8;  // 16-byte pieces per query row
+  __shared__ AttSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[kHeadsPerWg * (D + 8)];
+  const WorkItem wi = work_item(n_splits, (p.n_heads + kHeadsPerWg - 1) / kHeadsPerWg);
+  const int t = wi.t, split = wi.split, hg = wi.hg;
+  const int tid = threadIdx.x;
+  const int row_begin = split * tiles_per_split * kRT;
+  int32_t pidx = 0;
+  if (tid < kRT)
+    pidx = p.sel_idx[(int64_t)t * p.sel_stride + min(row_begin + tid, p.sel_stride - 1)];
+  u32x4 qv = u32x4{0u, 0u, 0u, 0u};
+  const int hl = tid / QPR;
+  if (tid < kHeadsPerWg * QPR) {
+    const int hq = min(hg * kHeadsPerWg + hl, p.n_heads - 1);
+    qv = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)t * p.n_heads + hq) * D +
+                                         (tid - hl * QPR) * 8);
+  }
+  const TokMeta meta = load_meta<kModeGather, HAS_B>(p, t);
+  uint32_t flags = 0;
+  const SegDesc sd = token_rows<kModeGather, HAS_B>(p, meta, flags);
+  if (tid < kHeadsPerWg * QPR)
+    *reinterpret_cast<u32x4*>(&qlds[hl * (D + 8) + (tid - hl * QPR) * 8]) = qv;
+  if (split == 0 && hg == 0 && tid == 0) {
+    report(p.err, flags);
+    if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
+  }
+  const int n_rows = sd.alen + sd.blen;
+  const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
+  const bool copy_rows = p.copy_out != nullptr && hg == 0;
+  const bf16x8 qa_unused[KSQ] = {};
+  // the tile loop's first barrier also orders the query stores above
+  attend_tiles<D, kModeGather, HAS_B, 1024, true, false>(p, sm, t, hg, split, n_splits, row_begin,
+                                                         row_end, sd, pidx, nullptr, false,
+                                                         qa_unused, qlds, copy_rows);
+}
+
+// Select and attend in one kernel (decode step, CSA, small batches).  Every
+// workgroup of token t -- one per (row split, 16-head group) -- runs the
+// token's exact top-k (step_select: the fast select over the indexer's
+// candidate lists, select_token when it gives up), which lists the selected
+// block indices of its own split's rows in LDS; the queries, the row
+// metadata and the candidate lists are all in flight together before it.
+// The first tile's rows are then fetched straight from that list, with no
+// global handoff or kernel boundary between the two stages.  The select's
+// LDS is reused for the tiles.  Head-group-0 workgroups write the idx
+// entries of their rows; split 0 writes the count.
 constexpr int kFuseThreads = sel::kThreads;
 constexpr int kFuseMaxTiles = 4;  // tiles per split the fused kernel takes
 
 template <int D>
 union FusedSmem {
-  sel::SelShared s;
+  sel::SelShared<kFuseThreads> s;
+  sel::FastShared<kFuseThreads> f;
   AttSmem<D> a;
 };
 
-template <int D, bool HAS_B, int KP>
+template <int D, bool HAS_B>
 __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunch sl,
                                                                      AttendLaunch p,
                                                                      int tiles_per_split,
@@ -516,11 +586,9 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   const int tid = threadIdx.x;
   const int row_begin = split * tiles_per_split * kRT;
 
-  // The queries of the 16 heads (clamped to the last real head) and the row
-  // metadata are loaded before the select, which hides their latency.
   u32x4 qv = u32x4{0u, 0u, 0u, 0u};
+  const int hl = tid / QPR;
   if (tid < kHeadsPerWg * QPR) {
-    const int hl = tid / QPR;
     const int hq = min(hg * kHeadsPerWg + hl, p.n_heads - 1);
     qv = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)t * p.n_heads + hq) * D +
                                          (tid - hl * QPR) * 8);
@@ -533,17 +601,14 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
   }
 
   const uint32_t win = (uint32_t)(tiles_per_split * kRT);  // this split's rows
-  const sel::SelResult r = sel::select_token<KP>(
+  const sel::SelResult r = sel::step_select<kFuseThreads>(
       sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.seq_kv[t],
-      sl.k_rows, sl.top_k,
-      sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
+      sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
-      sl.blocks_per_group, u.s, selrow, (uint32_t)row_begin, (uint32_t)row_begin + win);
+      sl.blocks_per_group, u.f, u.s, selrow, (uint32_t)row_begin, (uint32_t)row_begin + win);
 
-  if (tid < kHeadsPerWg * QPR) {
-    const int hl = tid / QPR;
+  if (tid < kHeadsPerWg * QPR)
     *reinterpret_cast<u32x4*>(&qlds[hl * (D + 8) + (tid - hl * QPR) * 8]) = qv;
-  }
   meta.a_cnt = (int32_t)r.emitted;
   uint32_t flags = 0;
   const SegDesc sd = token_rows<kModeGather, HAS_B>(p, meta, flags);
@@ -555,12 +620,10 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
     if ((uint32_t)tid < win && i < (uint32_t)sl.top_k)
       out[i] = i < r.emitted ? (r.listed ? selrow[tid] : (int32_t)i) : -1;
   }
-  if (split == 0 && hg == 0) {
-    if (tid == 0) {
-      sl.count[t] = (int32_t)r.emitted;
-      report(p.err, flags | r.flags);
-      if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
-    }
+  if (split == 0 && hg == 0 && tid == 0) {
+    sl.count[t] = (int32_t)r.emitted;
+    report(p.err, flags | r.flags);
+    if (p.n_kv_out != nullptr) p.n_kv_out[t] = sd.alen + sd.blen;
   }
   const int n_rows = sd.alen + sd.blen;
   const int row_end = min(row_begin + tiles_per_split * kRT, n_rows);
@@ -571,9 +634,11 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
       copy_rows);
 }
 
-// Merge of the split partials of one (token, head).  Wave w takes splits
-// w, w+4, ...; the first eight of each wave are loaded together with every
-// split's (max, sum), so two splits rounds cost one memory round trip.
+// Merge of the split partials of one (token, head): out = sum_s w_s o_s with
+// w_s = l_s e^{m_s - M} / (sum_s' l_s' e^{m_s' - M} [+ e^{sink - M}]), where
+// o_s is split s's normalised bf16 output.  Wave w takes splits w, w+4, ...;
+// the first eight of each wave are loaded together with every split's (max,
+// sum), so up to 32 splits cost one memory round trip.
 template <int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int n_splits) {
   constexpr int EPL = D / 64;  // output elements per lane
@@ -584,11 +649,12 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int
   __shared__ __attribute__((aligned(16))) float red[SG][D];
   const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const float* part_o = static_cast<const float*>(p.ws);
-  const float* part_ml = part_o + (size_t)p.T * n_splits * p.n_heads * D;
+  const float* part_ml = static_cast<const float*>(p.ws);
+  const uint16_t* part_o =
+      reinterpret_cast<const uint16_t*>(part_ml + part_ml_floats(p.T, n_splits, p.n_heads));
   const size_t slot0 = (size_t)t * n_splits * p.n_heads + h;
   const size_t sstride = (size_t)p.n_heads * D;
-  const float* pbase = part_o + slot0 * D + lane * EPL;
+  const uint16_t* pbase = part_o + slot0 * D + lane * EPL;
 
   float m_s = -INFINITY, l_s = 0.f;
   if (tid < n_splits) {
@@ -604,19 +670,20 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int
 #pragma unroll
       for (int j = 0; j < EPL; ++j) v[c][j] = 0.f;
       if (s < n_splits) {
-        const float* src = pbase + (size_t)s * sstride;
-        if constexpr (EPL % 4 == 0) {
+        const uint16_t* src = pbase + (size_t)s * sstride;
+        if constexpr (EPL % 8 == 0) {
 #pragma unroll
-          for (int j = 0; j < EPL; j += 4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(src + j);
-            v[c][j] = x[0];
-            v[c][j + 1] = x[1];
-            v[c][j + 2] = x[2];
-            v[c][j + 3] = x[3];
+          for (int j = 0; j < EPL; j += 8) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(src + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[c][j + 2 * e] = __uint_as_float(x[e] << 16);
+              v[c][j + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+            }
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < EPL; ++j) v[c][j] = src[j];
+          for (int j = 0; j < EPL; ++j) v[c][j] = bf16_to_f32(src[j]);
         }
       }
     }
@@ -632,9 +699,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int
     s2 = p.sink[h] * kLog2e;
     M = fmaxf(M, s2);
   }
-  const float f = (l_s > 0.f) ? exp2f(m_s - M) : 0.f;
+  const float f = (l_s > 0.f) ? l_s * exp2f(m_s - M) : 0.f;
   fw[tid] = f;
-  const float Lp = wave_sum_f32(l_s * f);
+  const float Lp = wave_sum_f32(f);
   if (lane == 0) wred[1][wave] = Lp;
   __syncthreads();
   float Lsum = wred[1][0] + wred[1][1] + wred[1][2] + wred[1][3];
@@ -668,9 +735,16 @@ struct SplitPlan {
   int tiles_per_split, n_splits;
 };
 
-SplitPlan plan_splits(int T, int n_heads, int max_rows) {
+// Row splits of a launch: split_tiles tiles per split when the caller fixes it
+// (the decode step), else enough splits for about 256 workgroups.
+SplitPlan plan_splits(int T, int n_heads, int max_rows, int split_tiles) {
   SplitPlan sp;
   const int n_tiles = max_rows > 0 ? (max_rows + kRT - 1) / kRT : 1;
+  if (split_tiles > 0) {
+    sp.tiles_per_split = split_tiles < n_tiles ? split_tiles : n_tiles;
+    sp.n_splits = (n_tiles + sp.tiles_per_split - 1) / sp.tiles_per_split;
+    if (sp.n_splits <= kMaxSplits) return sp;
+  }
   const int n_hg = (n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
   int want = (256 + T * n_hg - 1) / (T * n_hg);
   if (want < 1) want = 1;
@@ -683,7 +757,7 @@ SplitPlan plan_splits(int T, int n_heads, int max_rows) {
 
 template <int D>
 hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
-  const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
+  const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows, a.split_tiles);
   const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
   dim3 grid((unsigned)(sp.n_splits * n_hg * a.T));
   const int mode = a.sel_idx != nullptr ? kModeGather
@@ -693,7 +767,12 @@ hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL((attend_split_kernel<D, MODE, HB>), grid, dim3(256), 0, s, a,          \
                      sp.tiles_per_split, sp.n_splits)
   if (mode == kModeGather) {
-    if (a.kv_b != nullptr) CSA_SPLIT(kModeGather, true); else CSA_SPLIT(kModeGather, false);
+    if (a.kv_b != nullptr)
+      hipLaunchKernelGGL((gather_attend_kernel<D, true>), grid, dim3(1024), 0, s, a,
+                         sp.tiles_per_split, sp.n_splits);
+    else
+      hipLaunchKernelGGL((gather_attend_kernel<D, false>), grid, dim3(1024), 0, s, a,
+                         sp.tiles_per_split, sp.n_splits);
   } else if (mode == kModeVisible) {
     if (a.kv_b != nullptr) CSA_SPLIT(kModeVisible, true); else CSA_SPLIT(kModeVisible, false);
   } else {
@@ -717,18 +796,15 @@ bool fused_fits(const SplitPlan& sp, int T, int n_heads) {
 
 template <int D>
 hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStream_t s) {
-  const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows);
+  const SplitPlan sp = plan_splits(a.T, a.n_heads, a.max_rows, a.split_tiles);
   const int n_hg = (a.n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
   dim3 grid((unsigned)(sp.n_splits * n_hg * a.T));
-#define CSA_FUSED(HB, KP)                                                                  \
-  hipLaunchKernelGGL((select_attend_kernel<D, HB, KP>), grid, dim3(kFuseThreads), 0, s, sl, a, \
-                     sp.tiles_per_split, sp.n_splits)
-  if (sl.slots == 4) {
-    if (a.kv_b != nullptr) CSA_FUSED(true, 4); else CSA_FUSED(false, 4);
-  } else {
-    if (a.kv_b != nullptr) CSA_FUSED(true, sel::KPT); else CSA_FUSED(false, sel::KPT);
-  }
-#undef CSA_FUSED
+  if (a.kv_b != nullptr)
+    hipLaunchKernelGGL((select_attend_kernel<D, true>), grid, dim3(kFuseThreads), 0, s, sl, a,
+                       sp.tiles_per_split, sp.n_splits);
+  else
+    hipLaunchKernelGGL((select_attend_kernel<D, false>), grid, dim3(kFuseThreads), 0, s, sl, a,
+                       sp.tiles_per_split, sp.n_splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.n_splits == 1) return e;
   hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),
@@ -738,13 +814,13 @@ hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStre
 
 }  // namespace
 
-bool select_attend_fits(int T, int n_heads, int max_rows) {
-  return T > 0 && fused_fits(plan_splits(T, n_heads, max_rows), T, n_heads);
+bool select_attend_fits(int T, int n_heads, int max_rows, int split_tiles) {
+  return T > 0 && fused_fits(plan_splits(T, n_heads, max_rows, split_tiles), T, n_heads);
 }
 
 hipError_t launch_select_attend(const SelectLaunch& sl, const AttendLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (!select_attend_fits(a.T, a.n_heads, a.max_rows) || a.sel_stride != sl.top_k)
+  if (!select_attend_fits(a.T, a.n_heads, a.max_rows, a.split_tiles) || a.sel_stride != sl.top_k)
     return hipErrorInvalidValue;
   switch (a.head_dim) {
     case 64: return launch_fused_d<64>(sl, a, s);
@@ -755,11 +831,11 @@ hipError_t launch_select_attend(const SelectLaunch& sl, const AttendLaunch& a, h
   }
 }
 
-size_t attend_ws_bytes(int T, int n_heads, int head_dim, int max_rows) {
-  const SplitPlan sp = plan_splits(T, n_heads, max_rows);
+size_t attend_ws_bytes(int T, int n_heads, int head_dim, int max_rows, int split_tiles) {
+  const SplitPlan sp = plan_splits(T, n_heads, max_rows, split_tiles);
   if (sp.n_splits == 1) return 256;
   const size_t n = (size_t)T * sp.n_splits * n_heads;
-  size_t b = n * head_dim * 4 + n * 2 * 4;
+  size_t b = part_ml_floats(T, sp.n_splits, n_heads) * 4 + n * head_dim * 2;
   return (b + 255) & ~(size_t)255;
 }
 

@@ -325,6 +325,9 @@ __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const 
 // ---------------------------------------------------------------------------
 // Internal launchers (host).  Arguments are validated by the C ABI layer.
 // ---------------------------------------------------------------------------
+// Keys the decode step's select holds: four register slots per thread of a
+// 1024-thread workgroup (the fast select's capacity).
+constexpr int kStepPool = 4096;
 struct IndexScoreLaunch {
   const uint16_t* q_idx; const float* w; const uint16_t* k_idx; int64_t k_rows;
   const int64_t* pos; const int64_t* seq_kv; const int32_t* n_comp;
@@ -350,7 +353,9 @@ struct TopkPlan {
   int list_len;                          // keys per group list (0: no lists)
   int groups_per_token, blocks_per_group;
 };
-TopkPlan plan_topk(int T, int64_t ld, int top_k);
+// pool: keys the select holds in registers (kPoolCap for the top-k kernel,
+// kStepPool in the decode step)
+TopkPlan plan_topk(int T, int64_t ld, int top_k, int pool);
 struct TopkWs {
   uint64_t* cand;  // [T, groups_per_token, list_len]
   uint64_t* gcut;  // [T, groups_per_token]
@@ -394,25 +399,33 @@ struct AttendLaunch {
   int b_cap;                              // gather mode: at most this many B rows
   uint16_t* copy_out; int64_t copy_stride; int32_t* n_kv_out;
   int max_rows;
+  int split_tiles;                        // 64-row tiles per row split (0: planned for ~256 workgroups)
   uint16_t* out; float* lse;
   void* ws; uint32_t* err;
 };
-size_t attend_ws_bytes(int T, int n_heads, int head_dim, int max_rows);
+// Rows per split of the decode step's attention: one 64-row tile per
+// workgroup, so that each fetches its rows in one round trip; the bf16 split
+// partials of all splits are then about as large as the rows themselves.
+constexpr int kStepSplitTiles = 1;
+size_t attend_ws_bytes(int T, int n_heads, int head_dim, int max_rows, int split_tiles);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 
-// Top-k and gather-mode attention in one kernel (decode step, CSA).  The
-// attention half takes its selection from the select, not from sel_idx /
-// sel_cnt; idx and count are still written.
+// The decode step's top-k (S2) over the indexer's scores and candidate lists:
+// either inside the attention kernel (select_attend_kernel: every workgroup of
+// a token selects, then attends over its own share of the selected rows) or,
+// for larger batches, in a select kernel of one workgroup per token followed
+// by the gather-mode attention kernel.
 struct SelectLaunch {
   const float* scores; int64_t ld; const int64_t* pos; const int32_t* n_comp;
   const int64_t* seq_kv; int64_t k_rows;  // the indexer's key range check
   int ratio, top_k;
   const uint64_t* cand; const uint64_t* gcut;
   int list_len, groups_per_token, blocks_per_group;
-  int slots;  // select_slots() of the plan
   int32_t* idx; int32_t* count;
+  uint32_t* err;
 };
-bool select_attend_fits(int T, int n_heads, int max_rows);
+bool select_attend_fits(int T, int n_heads, int max_rows, int split_tiles);
 hipError_t launch_select_attend(const SelectLaunch& s, const AttendLaunch& a, hipStream_t st);
+hipError_t launch_step_select(const SelectLaunch& s, int T, hipStream_t st);
 
 }  // namespace csa

@@ -18,10 +18,10 @@ __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
     int ratio, int top_k, const uint64_t* __restrict__ cand_all, const uint64_t* __restrict__ gcut_all, int list_len,
     int groups_per_token, int blocks_per_group, int32_t* __restrict__ idx,
     int32_t* __restrict__ count, uint32_t* __restrict__ err) {
-  __shared__ sel::SelShared sh;
+  __shared__ sel::SelShared<sel::kThreads> sh;
   const int tid = threadIdx.x;
   const int t = blockIdx.x;
-  const sel::SelResult r = sel::select_token<KP>(
+  const sel::SelResult r = sel::select_token<sel::kThreads, KP>(
       scores + (int64_t)t * ld, ld, pos[t], n_comp[t], ratio,
       seq_kv != nullptr ? seq_kv[t] : 0, seq_kv != nullptr ? k_rows : INT64_MAX, top_k, cand_all + (int64_t)t * groups_per_token * list_len, gcut_all + (int64_t)t * groups_per_token,
       list_len, groups_per_token, blocks_per_group, sh, sh.outl, 0u, (uint32_t)top_k);
@@ -32,6 +32,31 @@ __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
   if (tid == 0) {
     count[t] = (int32_t)r.emitted;
     report(err, r.flags);
+  }
+}
+
+// The decode step's top-k for larger batches: one workgroup per token, the
+// fast select (select_token when it gives up), the selection written straight
+// to idx in ascending block order and padded with -1.
+__global__ __launch_bounds__(sel::kThreads) void step_select_kernel(SelectLaunch sl) {
+  __shared__ union {
+    sel::SelShared<sel::kThreads> s;
+    sel::FastShared<sel::kThreads> f;
+  } u;
+  const int t = blockIdx.x;
+  int32_t* out = sl.idx + (int64_t)t * sl.top_k;
+  const sel::SelResult r = sel::step_select<sel::kThreads>(
+      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.seq_kv[t],
+      sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
+      sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
+      sl.blocks_per_group, u.f, u.s, out, 0u, (uint32_t)sl.top_k);
+  for (uint32_t i = threadIdx.x; i < (uint32_t)sl.top_k; i += sel::kThreads) {
+    if (i >= r.emitted) out[i] = -1;
+    else if (!r.listed) out[i] = (int32_t)i;
+  }
+  if (threadIdx.x == 0) {
+    sl.count[t] = (int32_t)r.emitted;
+    report(sl.err, r.flags);
   }
 }
 
@@ -79,33 +104,36 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
 
 }  // namespace
 
-TopkPlan plan_topk(int T, int64_t ld, int top_k) {
+TopkPlan plan_topk(int T, int64_t ld, int top_k, int pool) {
   const IndexPlan ip = plan_index(T, ld);
   TopkPlan p{};
   p.waves_per_token = ip.waves_per_token();
   p.blocks_per_wave = ip.blocks_per_wave();
   // Short rows select over all their blocks.  Rows with more groups than the
   // select holds bounds for take its global path.
-  if (ld <= kPoolCap || p.waves_per_token > kMaxGroups) return p;
-  // every wave keeps its share of the select's key set
-  int m = kPoolCap / p.waves_per_token;
-  if (m > 32) m = 32;
-  if (m < 1) m = 1;
-  p.wave_m = m;
-  // A workgroup merges its waves' lists into one of 16 keys when they fit one
-  // wave and the token's merged lists still hold at least three times top_k
-  // keys.  The select then holds a third as many keys, and a group's expected
-  // share of a full row's top-k is at most 16/3 keys, well inside its list.
-  if (kIndexWaves * m <= 64 && (int64_t)ip.wgs_per_token * kMergedLen >= 3 * (int64_t)top_k) {
+  if (ld <= pool || p.waves_per_token > kMaxGroups) return p;
+  // A workgroup merges its waves' lists into one of 16 keys when the token's
+  // merged lists fit the pool and still hold at least three times top_k
+  // keys: a group's expected share of a full row's top-k is then at most
+  // 16/3 keys, well inside its list.  Each wave keeps its top 8 for the
+  // merge, which bounds the group's unlisted blocks tightly.
+  const int64_t merged = (int64_t)ip.wgs_per_token * kMergedLen;
+  if (merged <= pool && merged >= 3 * (int64_t)top_k) {
+    p.wave_m = kMergeMaxWaveM;
     p.merge = 1;
     p.list_len = kMergedLen;
     p.groups_per_token = ip.wgs_per_token;
     p.blocks_per_group = kIndexWaves * p.blocks_per_wave;
-  } else {
-    p.list_len = m;
-    p.groups_per_token = p.waves_per_token;
-    p.blocks_per_group = p.blocks_per_wave;
+    return p;
   }
+  // otherwise every wave keeps its share of the select's key set
+  int m = pool / p.waves_per_token;
+  if (m > 32) m = 32;
+  if (m < 1) m = 1;
+  p.wave_m = m;
+  p.list_len = m;
+  p.groups_per_token = p.waves_per_token;
+  p.blocks_per_group = p.blocks_per_wave;
   return p;
 }
 
@@ -147,6 +175,12 @@ hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* po
   dim3 grid((unsigned)(p.waves_per_token / kIndexWaves), (unsigned)T);
   hipLaunchKernelGGL(score_cands_kernel, grid, dim3(kCandThreads), 0, s, scores, ld, pos, n_comp,
                      ratio, p.blocks_per_wave, cand_args(p, ws), err);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_select(const SelectLaunch& sl, int T, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(step_select_kernel, dim3((unsigned)T), dim3(sel::kThreads), 0, s, sl);
   return hipGetLastError();
 }
 

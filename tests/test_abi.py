@@ -132,8 +132,10 @@ def test_decode_step_validation(lib):
     a.top_k = 0
     assert st(FAKE, need) == b.CSA_EINVAL
     a.top_k = 1024
-    a.all_kv = None
+    a.all_kv = FAKE + 2  # all_kv is optional, but must be 16-byte aligned when given
     assert st(FAKE, need) == b.CSA_EINVAL
+    a.all_kv = None
+    assert b.csa_decode_step_workspace_bytes(a) == need
     a.all_kv = FAKE
     a.head_dim = 100
     assert st(FAKE, need) == b.CSA_EUNSUPPORTED

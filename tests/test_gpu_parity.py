@@ -367,7 +367,7 @@ def test_decode_step_hca_1m(dev):
         setattr(a, k, v.data_ptr())
     a.comp_rows, a.swa_rows = h.comp_kv.shape[0], h.swa.shape[0]
     a.out, a.lse, a.err = out.data_ptr(), lse.data_ptr(), err.data_ptr()
-    ws = torch.empty(max(B().csa_decode_step_workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
+    ws = B().step_workspace(a, dev)
     B().csa_decode_step(a, ws)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
@@ -389,7 +389,7 @@ def test_csa_equals_hca_when_all_selected(dev):
     outs = {"out": torch.zeros((1, 16, 128), dtype=torch.bfloat16, device=dev),
             "err": _err(dev)}
     a = B().step_args(inp, d, outs, mode=B().CSA_MODE_HCA, max_vis=250)
-    ws = torch.empty(max(B().csa_decode_step_workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
+    ws = B().step_workspace(a, dev)
     B().csa_decode_step(a, ws)
     hca = outs["out"].float().cpu().numpy()[0]
     ref, _ = hca_token(inp.q[0], inp.comp_kv, 250, inp.swa[:32], inp.scale)
