@@ -81,6 +81,42 @@ csa_status csa_index_score(const uint16_t* q_idx, const float* w,
                            float* scores, int64_t ld, uint32_t* err, void* stream);
 
 /*
+ * S1 with narrow keys (post-probe audit, C4; 1M-context audit, M1/A2: indexer
+ * keys and queries stored and multiplied in an 8-bit floating-point format).
+ * q_idx [T, n_ih, ihd] and k_idx [k_rows, ihd] are OCP FP8 E4M3 codes (one
+ * byte each: sign, 4 exponent bits with bias 7, 3 mantissa bits) with one
+ * power-of-two scale per query head, q_scale [T, n_ih] fp32, and per key
+ * block, k_scale [k_rows] fp32 (as csa_quantize_e4m3 makes them).  The score
+ * is S1's formula on the dequantised values:
+ *     scores[t, s] = sum_h w[t,h] * max(0, (q_scale[t,h] q[t,h]) . (k_scale[r] k[r])),
+ *     r = seq_kv[t] + s,
+ * computed as k_scale[r] * sum_h (w[t,h] q_scale[t,h]) * max(0, q[t,h] . k[r]) with
+ * FP8 matrix products (exact products, fp32 sums).  Everything else --
+ * visibility, layout of scores, errors, supported shapes -- is as for
+ * csa_index_score; q_idx and k_idx must be 16-byte aligned.  The key stream
+ * is half the bf16 one.
+ */
+csa_status csa_index_score_e4m3(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                const uint8_t* k_idx, const float* k_scale, int64_t k_rows,
+                                const int64_t* pos, const int64_t* seq_kv, const int32_t* n_comp,
+                                int T, int n_ih, int ihd, int ratio,
+                                float* scores, int64_t ld, uint32_t* err, void* stream);
+
+/*
+ * Quantisation of bf16 rows to E4M3 codes for csa_index_score_e4m3 (the
+ * post-probe audit's C4 cache format; the write side of the indexer-key
+ * cache).  For each row i of src [rows, d]: scale[i] = 2**e for the smallest
+ * e with max_j |src[i,j]| * 2**-e <= 448 (E4M3's largest finite value;
+ * 1 for a zero row), and codes[i, j] = src[i, j] * 2**-e rounded to the
+ * nearest E4M3 value, ties to even (subnormals included).  The codes are a
+ * function of the inputs alone (a power-of-two scale is exact).
+ *   src [rows, d] bf16   codes [rows, d] uint8   scale [rows] fp32
+ * Supported: 1 <= d <= 512, rows >= 0.
+ */
+csa_status csa_quantize_e4m3(const uint16_t* src, int64_t rows, int d, uint8_t* codes,
+                             float* scale, void* stream);
+
+/*
  * S2 -- causal top-k (post-probe audit, F3: tk = min(top_k, n_comp), topk over
  * the scores; PART A suspect 3: only blocks before the query's own block).
  * For each token, k_eff = min(top_k, n_vis[t]) indices s < n_vis[t] of the
@@ -151,8 +187,17 @@ csa_status csa_mqa_attend(const uint16_t* q, int T, int n_heads, int head_dim,
  * S5 -- one decode step of one attention layer, all stages enqueued on one
  * stream with no host synchronisation (capturable in a HIP graph).
  *
- * mode CSA_MODE_CSA: S1 -> S2 -> S3 -> S4 over all_kv (selected compressed rows,
- *   then SWA rows).  Requires q_idx, w, k_idx, all_kv.
+ * mode CSA_MODE_CSA: S1 -> S2 -> S3 -> S4 over the selected compressed rows,
+ *   then the SWA rows.  Requires q_idx, w, k_idx.  The rows are read in place
+ *   (the selected ones through their block indices); all_kv, when given,
+ *   also receives them in that order -- the preallocated gather buffer of the
+ *   post-probe audit's C2 -- and may be NULL (1M-context audit, M5/A9: the
+ *   attention reads the two buffers directly).
+ *   With idx_e4m3 = 1, S1 scores E4M3 copies of the indexer queries and keys
+ *   (post-probe audit, C4: narrow storage paired with narrow products; the
+ *   1M-context audit's A2 gates it on top-k recall against a full-precision
+ *   indexer) and S2 keeps the best C of them, whose bf16 scores then decide
+ *   the top_k (see the idx_e4m3 fields).
  * mode CSA_MODE_HCA (1M-context audit, D4): no indexer; S4 over the entire
  *   visible compressed history comp_kv[seq_kv[t] .. +n_vis[t]-1] followed by
  *   the SWA rows, read in place (no concatenation).
@@ -168,9 +213,9 @@ typedef struct csa_step_args {
   int T, n_ih, ihd, ratio, top_k, window, n_heads, head_dim;
   int64_t max_vis;
   float scale;
-  const uint16_t* q_idx;    /* [T, n_ih, ihd]        (CSA) */
+  const uint16_t* q_idx;    /* [T, n_ih, ihd] bf16   (CSA) */
   const float* w;           /* [T, n_ih]             (CSA) */
-  const uint16_t* k_idx;    /* [k_rows, ihd]         (CSA) */
+  const uint16_t* k_idx;    /* [k_rows, ihd] bf16    (CSA) */
   int64_t k_rows;
   const uint16_t* comp_kv;  /* [comp_rows, head_dim] */
   int64_t comp_rows;
@@ -183,7 +228,7 @@ typedef struct csa_step_args {
   const int32_t* n_comp;    /* [T] */
   const int64_t* swa_row0;  /* [T] */
   const int32_t* swa_len;   /* [T] */
-  uint16_t* all_kv;         /* [T, top_k + window, head_dim]  (CSA, required) */
+  uint16_t* all_kv;         /* [T, top_k + window, head_dim] or NULL  (CSA) */
   uint16_t* out;            /* [T, n_heads, head_dim] (required) */
   float* lse;               /* [T, n_heads] or NULL  */
   float* scores;            /* [T, max_vis] or NULL  */
@@ -191,6 +236,18 @@ typedef struct csa_step_args {
   int32_t* count;           /* [T] or NULL           */
   int32_t* n_kv;            /* [T] or NULL           */
   uint32_t* err;            /* device word or NULL   */
+  /* CSA mode, idx_e4m3 = 1: the indexer streams E4M3 copies of its queries
+     and keys instead (q_idx8 [T, n_ih, ihd] with q_idx_scale [T, n_ih],
+     k_idx8 [k_rows, ihd] with k_idx_scale [k_rows]; see csa_quantize_e4m3)
+     and keeps the C = min(top_k + top_k/2, 4096) blocks with the largest
+     E4M3 scores (lower index first on ties); the top_k of those C by their
+     bf16 scores (q_idx, k_idx: still required) are selected.  `scores`
+     receives the E4M3 scores.  idx_e4m3 = 0: the five fields are ignored. */
+  int idx_e4m3;
+  const uint8_t* q_idx8;
+  const float* q_idx_scale;
+  const uint8_t* k_idx8;
+  const float* k_idx_scale;
 } csa_step_args;
 
 size_t csa_decode_step_workspace_bytes(const csa_step_args* a);

@@ -28,7 +28,8 @@ import math
 
 import numpy as np
 
-from .csa_oracle import indexer_scores
+from .csa_oracle import (bf16_to_f64, gather_rows, indexer_scores, select_top_blocks,
+                         shared_kv_attention, visible_blocks)
 
 E4M3_MAX = 448.0
 
@@ -142,3 +143,42 @@ def indexer_scores_e4m3(q_codes: np.ndarray, q_scale: np.ndarray, w: np.ndarray,
     q = e4m3_to_f64(q_codes) * np.asarray(q_scale, dtype=np.float64)[:, None]
     k = e4m3_to_f64(k_codes) * np.asarray(k_scale, dtype=np.float64)[:, None]
     return indexer_scores(q, w, k)
+
+
+def prefilter_count(top_k: int) -> int:
+    """Candidates the E4M3 prefilter keeps: half as many again as top_k (at
+    most 4096).  A reading of [P1] C4 with [P2] A2's recall gate: narrow
+    products rank the blocks, and the full-precision scores of a margin of
+    candidates around the top_k decide the selection."""
+    return min(int(top_k) + int(top_k) // 2, 4096)
+
+
+def select_prefiltered(I8: np.ndarray, I: np.ndarray, top_k: int, C: int):
+    """The min(top_k, n) blocks with the largest bf16 scores I among the
+    min(C, n) blocks with the largest E4M3 scores I8; both orders take the
+    lower block index first on equal scores.  Returns (selection in
+    descending I order, candidates in ascending block order)."""
+    cand = np.sort(select_top_blocks(I8, C))
+    inner = select_top_blocks(np.asarray(I, dtype=np.float64)[cand], top_k)
+    return cand[inner], cand
+
+
+def csa_token_e4m3(inp, t: int, sink=None) -> dict:
+    """The CSA decode path for token t with the E4M3 indexer prefilter: the
+    token's indexer queries and its visible keys quantised row by row, scored
+    (scores8), the prefilter_count(top_k) best kept, their bf16 scores
+    deciding the top_k; gather and attention as in csa_token."""
+    row0 = int(inp.seq_kv[t])
+    n_vis = visible_blocks(int(inp.pos[t]), inp.ratio, int(inp.n_comp[t]))
+    q = bf16_to_f64(inp.q_idx[t])
+    keys = bf16_to_f64(inp.k_idx[row0:row0 + n_vis])
+    qc, qs = quantize_rows_e4m3(q)
+    kc, ks = quantize_rows_e4m3(keys)
+    I8, A8 = indexer_scores_e4m3(qc, qs, inp.w[t], kc, ks)
+    I, A = indexer_scores(q, inp.w[t], keys)
+    sel, cand = select_prefiltered(I8, I, inp.top_k, prefilter_count(inp.top_k))
+    s0, sl = int(inp.swa_row0[t]), int(inp.swa_len[t])
+    rows_bits = gather_rows(inp.comp_kv[row0:row0 + n_vis], sel, inp.swa[s0:s0 + sl])
+    out, lse = shared_kv_attention(bf16_to_f64(inp.q[t]), bf16_to_f64(rows_bits), inp.scale, sink)
+    return dict(n_vis=n_vis, scores8=I8, scale_A8=A8, scores=I, scale_A=A, cand=cand, sel=sel,
+                rows=rows_bits, out=out, lse=lse)

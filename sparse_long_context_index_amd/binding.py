@@ -45,6 +45,8 @@ class StepArgs(ctypes.Structure):
         ("q", _vp), ("sink", _vp), ("pos", _vp), ("seq_kv", _vp), ("n_comp", _vp),
         ("swa_row0", _vp), ("swa_len", _vp), ("all_kv", _vp), ("out", _vp), ("lse", _vp),
         ("scores", _vp), ("idx", _vp), ("count", _vp), ("n_kv", _vp), ("err", _vp),
+        ("idx_e4m3", _i32), ("q_idx8", _vp), ("q_idx_scale", _vp), ("k_idx8", _vp),
+        ("k_idx_scale", _vp),
     ]
 
 
@@ -53,6 +55,9 @@ _SIGS = {
     "csa_abi_version": (_i32, []),
     "csa_index_score": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                _vp, _i64, _vp, _vp]),
+    "csa_index_score_e4m3": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32,
+                                    _i32, _i32, _vp, _i64, _vp, _vp]),
+    "csa_quantize_e4m3": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "csa_topk_workspace_bytes": (_sz, [_i32, _i64, _i32]),
     "csa_topk": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp, _vp]),
     "csa_gather": (_i32, [_vp, _i64, _vp, _vp, _vp, _i32, _vp, _i64, _vp, _vp, _i32, _i32, _i32,
@@ -130,6 +135,27 @@ def csa_index_score(q_idx, w, k_idx, pos, seq_kv, n_comp, n_ih, ihd, ratio, scor
         _p(n_comp, (torch.int32,), "n_comp"), T, n_ih, ihd, ratio,
         _p(scores, (torch.float32,), "scores"), ld, _p(err, (torch.int32,), "err", True),
         _stream(stream)))
+
+
+def csa_index_score_e4m3(q_idx, q_scale, w, k_idx, k_scale, pos, seq_kv, n_comp, n_ih, ihd,
+                         ratio, scores, ld, err=None, stream=None):
+    T = int(pos.shape[0])
+    _check("csa_index_score_e4m3", load().csa_index_score_e4m3(
+        _p(q_idx, (torch.uint8,), "q_idx"), _p(q_scale, (torch.float32,), "q_scale"),
+        _p(w, (torch.float32,), "w"), _p(k_idx, (torch.uint8,), "k_idx"),
+        _p(k_scale, (torch.float32,), "k_scale"), int(k_idx.shape[0]),
+        _p(pos, (torch.int64,), "pos"), _p(seq_kv, (torch.int64,), "seq_kv"),
+        _p(n_comp, (torch.int32,), "n_comp"), T, n_ih, ihd, ratio,
+        _p(scores, (torch.float32,), "scores"), ld,
+        _p(err, (torch.int32, torch.uint32), "err", optional=True), _stream(stream)))
+
+
+def csa_quantize_e4m3(src, codes, scale, stream=None):
+    """src [rows, d] bf16 -> codes [rows, d] uint8 (E4M3), scale [rows] fp32."""
+    rows, d = int(src.shape[0]), int(src.shape[1]) if src.dim() > 1 else 1
+    _check("csa_quantize_e4m3", load().csa_quantize_e4m3(
+        _p(src, _BF16, "src"), rows, d, _p(codes, (torch.uint8,), "codes"),
+        _p(scale, (torch.float32,), "scale"), _stream(stream)))
 
 
 def csa_topk_workspace_bytes(T, ld, top_k) -> int:
@@ -213,8 +239,24 @@ def upload(inp, dev) -> dict:
     return d
 
 
+def quantize_indexer_e4m3(d: dict, stream=None) -> dict:
+    """E4M3 codes and scales of the uploaded indexer queries and keys, made on
+    the GPU by csa_quantize_e4m3 (q_idx8, q_scale [T, n_ih], k_idx8, k_scale)."""
+    q, k = d["q_idx"], d["k_idx"]
+    T, n_ih, ihd = q.shape
+    q8 = torch.empty((T, n_ih, ihd), dtype=torch.uint8, device=q.device)
+    qs = torch.empty((T, n_ih), dtype=torch.float32, device=q.device)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=k.device)
+    ks = torch.empty(k.shape[0], dtype=torch.float32, device=k.device)
+    csa_quantize_e4m3(q.reshape(T * n_ih, ihd), q8.view(T * n_ih, ihd), qs.view(-1), stream)
+    csa_quantize_e4m3(k, k8, ks, stream)
+    d = dict(d)
+    d.update(q_idx8=q8, q_scale=qs, k_idx8=k8, k_scale=ks)
+    return d
+
+
 def step_args(inp, d: dict, outs: dict, mode: int = CSA_MODE_CSA, max_vis: Optional[int] = None,
-              sink: Optional[torch.Tensor] = None) -> StepArgs:
+              sink: Optional[torch.Tensor] = None, e4m3: bool = False) -> StepArgs:
     """Pack a csa_step_args for a CSAInputs batch whose tensors are in `d`
     (see upload) and whose outputs are in `outs` (all_kv, out, lse, scores,
     idx, count, n_kv, err; any may be absent)."""
@@ -234,6 +276,10 @@ def step_args(inp, d: dict, outs: dict, mode: int = CSA_MODE_CSA, max_vis: Optio
     a.swa_row0, a.swa_len = ptr(d["swa_row0"]), ptr(d["swa_len"])
     for k in ("all_kv", "out", "lse", "scores", "idx", "count", "n_kv", "err"):
         setattr(a, k, ptr(outs.get(k)))
+    if e4m3:
+        a.idx_e4m3 = 1
+        a.q_idx8, a.k_idx8 = ptr(d["q_idx8"]), ptr(d["k_idx8"])
+        a.q_idx_scale, a.k_idx_scale = ptr(d["q_scale"]), ptr(d["k_scale"])
     return a
 
 
@@ -257,11 +303,16 @@ def alloc_step_outputs(inp, dev, max_vis: Optional[int] = None, keep=True,
     return o
 
 
-def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None, all_kv: bool = True) -> dict:
-    """Upload a batch, run one csa_decode_step, return host copies."""
+def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None, all_kv: bool = True,
+                    e4m3: bool = False) -> dict:
+    """Upload a batch, run one csa_decode_step, return host copies (with
+    e4m3, the indexer queries and keys are quantised on the GPU first and
+    their codes and scales are returned too)."""
     d = upload(inp, dev)
+    if e4m3:
+        d = quantize_indexer_e4m3(d)
     outs = alloc_step_outputs(inp, dev, all_kv=all_kv)
-    a = step_args(inp, d, outs, sink=sink)
+    a = step_args(inp, d, outs, sink=sink, e4m3=e4m3)
     ws = step_workspace(a, dev)
     csa_decode_step(a, ws)
     torch.cuda.synchronize(dev)
@@ -273,4 +324,7 @@ def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None, all_kv: bool 
     }
     if all_kv:
         r["all_kv"] = res["all_kv"].view(torch.int16).numpy().view(np.uint16)
+    if e4m3:
+        for k in ("q_idx8", "q_scale", "k_idx8", "k_scale"):
+            r[k] = d[k].cpu().numpy()
     return r

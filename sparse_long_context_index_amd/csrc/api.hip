@@ -9,7 +9,7 @@ using namespace csa;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;  // 2: E4M3 indexer entry points and step fields
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxGridY = 65535;
 
@@ -81,8 +81,15 @@ csa_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 // Workspace of a decode step, in carve order.
 struct StepWs {
-  size_t scores, topk, idx, count, n_kv, attend, total;
+  size_t scores, topk, idx, count, n_kv, attend, pre_idx, pre_count, pre_key, pre_gcut, total;
 };
+
+// Candidates the E4M3 prefilter keeps: half as many again as top_k, at most
+// what the select holds in registers.
+int prefilter_count(int top_k) {
+  const int c = top_k + top_k / 2;
+  return c < kStepPool ? c : kStepPool;
+}
 
 StepWs step_ws_layout(const csa_step_args* a) {
   StepWs w{};
@@ -100,6 +107,17 @@ StepWs step_ws_layout(const csa_step_args* a) {
     if (!a->n_kv) off += align256((size_t)a->T * 4);
     w.attend = off;
     off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, a->top_k + a->window, kStepSplitTiles);
+    if (a->idx_e4m3) {
+      const size_t C = (size_t)prefilter_count(a->top_k);
+      w.pre_idx = off;
+      off += align256((size_t)a->T * C * 4);
+      w.pre_count = off;
+      off += align256((size_t)a->T * 4);
+      w.pre_key = off;
+      off += align256((size_t)a->T * C * 8);
+      w.pre_gcut = off;
+      off += align256((size_t)a->T * 8);
+    }
   } else {
     w.attend = off;
     const int64_t rows = a->max_vis + a->window;
@@ -135,6 +153,11 @@ csa_status check_step(const csa_step_args* a) {
       return CSA_EINVAL;
     if (a->ihd != 32 && a->ihd != 64 && a->ihd != 128) return CSA_EUNSUPPORTED;
     if (a->n_ih > 128 || a->top_k > kMaxTopk) return CSA_EUNSUPPORTED;
+    if (a->idx_e4m3 != 0 && a->idx_e4m3 != 1) return CSA_EINVAL;
+    if (a->idx_e4m3 && (!a->q_idx8 || !a->k_idx8 || !a->q_idx_scale || !a->k_idx_scale ||
+                        !aligned16(a->q_idx8) || !aligned16(a->k_idx8) ||
+                        !aligned4(a->q_idx_scale) || !aligned4(a->k_idx_scale)))
+      return CSA_EINVAL;
     if (a->max_vis > INT32_MAX) return CSA_EUNSUPPORTED;
   }
   return CSA_OK;
@@ -170,6 +193,34 @@ csa_status csa_index_score(const uint16_t* q_idx, const float* w, const uint16_t
   L.T = T; L.n_ih = n_ih; L.ihd = ihd; L.ratio = ratio;
   L.scores = scores; L.ld = ld; L.cand = CandArgs{}; L.err = err;
   return hip_status(launch_index_score(L, static_cast<hipStream_t>(stream)));
+}
+
+csa_status csa_index_score_e4m3(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                const uint8_t* k_idx, const float* k_scale, int64_t k_rows,
+                                const int64_t* pos, const int64_t* seq_kv, const int32_t* n_comp,
+                                int T, int n_ih, int ihd, int ratio, float* scores, int64_t ld,
+                                uint32_t* err, void* stream) {
+  csa_status s = check_index(reinterpret_cast<const uint16_t*>(q_idx), w,
+                             reinterpret_cast<const uint16_t*>(k_idx), k_rows, pos, seq_kv, n_comp,
+                             T, n_ih, ihd, ratio, scores, ld);
+  if (s != CSA_OK) return s;
+  if (!q_scale || !k_scale || !aligned4(q_scale) || !aligned4(k_scale)) return CSA_EINVAL;
+  if (T == 0) return CSA_OK;
+  IndexScoreLaunch L{};
+  L.q_idx = q_idx; L.w = w; L.k_idx = k_idx; L.k_rows = k_rows;
+  L.e4m3 = 1; L.q_scale = q_scale; L.k_scale = k_scale;
+  L.pos = pos; L.seq_kv = seq_kv; L.n_comp = n_comp;
+  L.T = T; L.n_ih = n_ih; L.ihd = ihd; L.ratio = ratio;
+  L.scores = scores; L.ld = ld; L.cand = CandArgs{}; L.err = err;
+  return hip_status(launch_index_score(L, static_cast<hipStream_t>(stream)));
+}
+
+csa_status csa_quantize_e4m3(const uint16_t* src, int64_t rows, int d, uint8_t* codes,
+                             float* scale, void* stream) {
+  if (rows < 0 || d < 1 || !src || !codes || !scale || !aligned4(scale)) return CSA_EINVAL;
+  if (d > 512) return CSA_EUNSUPPORTED;
+  if (rows == 0) return CSA_OK;
+  return hip_status(launch_quant_e4m3(src, rows, d, codes, scale, static_cast<hipStream_t>(stream)));
 }
 
 size_t csa_topk_workspace_bytes(int T, int64_t ld, int top_k) {
@@ -276,7 +327,13 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
 
   // S1 with its candidate lists
   IndexScoreLaunch I{};
-  I.q_idx = a->q_idx; I.w = a->w; I.k_idx = a->k_idx; I.k_rows = a->k_rows;
+  I.w = a->w; I.k_rows = a->k_rows;
+  if (a->idx_e4m3) {
+    I.q_idx = a->q_idx8; I.k_idx = a->k_idx8;
+    I.e4m3 = 1; I.q_scale = a->q_idx_scale; I.k_scale = a->k_idx_scale;
+  } else {
+    I.q_idx = a->q_idx; I.k_idx = a->k_idx;
+  }
   I.pos = a->pos; I.seq_kv = a->seq_kv; I.n_comp = a->n_comp;
   I.T = a->T; I.n_ih = a->n_ih; I.ihd = a->ihd; I.ratio = a->ratio;
   I.scores = scores; I.ld = a->max_vis;
@@ -301,6 +358,27 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
   S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
   S.idx = idx; S.count = count; S.err = a->err;
+  if (a->idx_e4m3) {
+    // E4M3 prefilter: the C best blocks by E4M3 score, rescored in bf16; they
+    // form one complete candidate list per token for the top-k below
+    const int C = prefilter_count(a->top_k);
+    SelectLaunch P = S;
+    P.top_k = C;
+    P.idx = reinterpret_cast<int32_t*>(base + lay.pre_idx);
+    P.count = reinterpret_cast<int32_t*>(base + lay.pre_count);
+    e = launch_step_select(P, a->T, st);
+    if (e != hipSuccess) return hip_status(e);
+    RescoreLaunch R{};
+    R.q_idx = a->q_idx; R.w = a->w; R.k_idx = a->k_idx; R.seq_kv = a->seq_kv;
+    R.idx = P.idx; R.count = P.count;
+    R.T = a->T; R.n_ih = a->n_ih; R.ihd = a->ihd; R.C = C;
+    R.key = reinterpret_cast<uint64_t*>(base + lay.pre_key);
+    R.gcut = reinterpret_cast<uint64_t*>(base + lay.pre_gcut);
+    e = launch_rescore(R, st);
+    if (e != hipSuccess) return hip_status(e);
+    S.cand = R.key; S.gcut = R.gcut; S.list_len = C;
+    S.groups_per_token = 1; S.blocks_per_group = (int)a->max_vis;
+  }
   if (select_attend_fits(a->T, a->n_heads, L.max_rows, L.split_tiles))
     return hip_status(launch_select_attend(S, L, st));
   e = launch_step_select(S, a->T, st);

@@ -329,7 +329,9 @@ __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const 
 // 1024-thread workgroup (the fast select's capacity).
 constexpr int kStepPool = 4096;
 struct IndexScoreLaunch {
-  const uint16_t* q_idx; const float* w; const uint16_t* k_idx; int64_t k_rows;
+  const void* q_idx; const float* w; const void* k_idx; int64_t k_rows;  // bf16, or E4M3 codes
+  int e4m3;                                  // 1: q_idx/k_idx are E4M3 codes scaled by
+  const float* q_scale; const float* k_scale;  // q_scale [T, n_ih] and k_scale [k_rows]
   const int64_t* pos; const int64_t* seq_kv; const int32_t* n_comp;
   int T, n_ih, ihd, ratio;
   float* scores; int64_t ld;
@@ -343,6 +345,20 @@ struct IndexPlan {
 };
 IndexPlan plan_index(int T, int64_t ld);
 hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s);
+// bf16 rescoring of candidate blocks (the E4M3 prefilter's): for token t and
+// j < count[t] (<= C), key[t*C + j] is the composite key of block
+// idx[t*C + j] with its bf16 indexer score; zero for count[t] <= j < C;
+// gcut[t] = 0, so that key[t*C ..] reads as one complete candidate list.
+struct RescoreLaunch {
+  const uint16_t* q_idx; const float* w; const uint16_t* k_idx; const int64_t* seq_kv;
+  const int32_t* idx; const int32_t* count;
+  int T, n_ih, ihd, C;
+  uint64_t* key; uint64_t* gcut;
+};
+hipError_t launch_rescore(const RescoreLaunch& a, hipStream_t s);
+// Row quantisation to E4M3 with one power-of-two scale per row (quant.hip).
+hipError_t launch_quant_e4m3(const uint16_t* src, int64_t rows, int d, uint8_t* codes,
+                             float* scale, hipStream_t s);
 
 // Top-k (see topk.hip).
 constexpr int kPoolCap = 12288;   // keys the select workgroup holds in registers

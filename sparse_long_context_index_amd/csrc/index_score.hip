@@ -35,6 +35,8 @@
 // Optionally the epilogue also emits the candidate lists of the top-k: each
 // wave's top-m composite selection keys (score, then lower block index),
 // merged per workgroup when the plan asks for it.
+#include <type_traits>
+
 #include "csa_common.h"
 
 namespace csa {
@@ -57,16 +59,25 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 
 // Up to 64 indexer heads the register budget is held to two waves per SIMD;
 // more heads need more registers and run one wave per SIMD.
-template <int IHD, int MT>
+//
+// F8: queries and keys are OCP FP8 E4M3 codes with one power-of-two scale per
+// query head (q_scale [T, n_ih]) and per key block (k_scale [rows]); the
+// products run on v_mfma_f32_32x32x16_fp8_fp8 (8 bytes of a row per lane and
+// k-step).  A positive per-block scale leaves every head's ReLU in place, so
+// I[s] = k_scale[s] * sum_h (w[h] q_scale[h]) ReLU(q8[h] . k8[s]): the query
+// scale folds into the head weight and the key scale multiplies the score.
+template <int IHD, int MT, bool F8>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? 2 : 1, 2))) void index_score_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ k_idx, int64_t k_rows,
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, int64_t k_rows,
     const int64_t* __restrict__ pos, const int64_t* __restrict__ seq_kv,
     const int32_t* __restrict__ n_comp, int n_ih, int ratio,
     float* __restrict__ scores, int64_t ld, CandArgs ca, uint32_t* __restrict__ err,
     int tiles_per_wave) {
-  constexpr int KS = IHD / 16;          // MFMA k-steps (one 16-byte chunk per lane each)
-  constexpr int CPR = IHD / 8;          // 16-byte chunks per key or query row
+  constexpr int KS = IHD / 16;          // MFMA k-steps of 16 elements
+  constexpr int RB = F8 ? IHD : 2 * IHD;  // bytes per key or query row
+  constexpr int CPR = RB / 16;          // 16-byte chunks per key or query row
   constexpr int TILE_CHUNKS = kTileN * CPR;
   constexpr int LPT = TILE_CHUNKS / 64; // DMA instructions per tile (1 KiB each)
   constexpr int QCHUNKS = MT * 32 * CPR;
@@ -82,7 +93,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const uint16_t* qt = q_idx + (int64_t)t * n_ih * IHD;
+  const uint8_t* qt = q_idx + (int64_t)t * n_ih * RB;
 
   // ---- one round trip: query block (to LDS), head weights, metadata ----
   // Query chunk e = row*CPR + p of the padded head block goes to LDS slot e,
@@ -94,16 +105,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     if (e0 + wave * 64 < QCHUNKS) {  // wave-uniform
       const int r = e / CPR, pp = e % CPR;
       const int hq = r < n_ih ? r : n_ih - 1;
-      lds_dma16(qt + (int64_t)hq * IHD + (pp ^ (r & (CPR - 1))) * 8, &qlds[e0 + wave * 64]);
+      lds_dma16(qt + (int64_t)hq * RB + (pp ^ (r & (CPR - 1))) * 16, &qlds[e0 + wave * 64]);
     }
   }
   // A operand of k-step s for lane (col, half): q[head = mt*32+col][16*s +
-  // 8*half .. +8]; accumulator element r of lane (col, half) is head
+  // 8*half .. +8] (bf16: 16 bytes, chunk 2s + half; E4M3: 8 bytes, half
+  // `half` of chunk s); accumulator element r of lane (col, half) is head
   // 8*(r/4) + 4*half + (r%4) of its 32-head tile.
-  auto q_operand = [&](int mt, int s) {
+  using Op = typename std::conditional<F8, uint2, u32x4>::type;  // one lane's MFMA operand
+  auto q_operand = [&](int mt, int s) -> Op {
     const int r = mt * 32 + col;
-    const int c = 2 * s + half;
-    return qlds[r * CPR + (c ^ (r & (CPR - 1)))];
+    if constexpr (F8) {
+      return reinterpret_cast<const uint2*>(qlds)[(r * CPR + (s ^ (r & (CPR - 1)))) * 2 + half];
+    } else {
+      const int c = 2 * s + half;
+      return qlds[r * CPR + (c ^ (r & (CPR - 1)))];
+    }
   };
   float wv[MT][16];
 #pragma unroll
@@ -111,7 +128,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      wv[mt][r] = w[(int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1)];
+      const int64_t hi = (int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1);
+      wv[mt][r] = F8 ? w[hi] * q_scale[hi] : w[hi];
     }
   }
   // The token metadata and the scalar arguments are read in the same batch
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   const int64_t tile_end = min(tile_begin + (int64_t)tiles_per_wave, n_tiles);
   const int64_t wave_in_token = (int64_t)blockIdx.x * kWaves + wave;
   const bool active = tile_begin < tile_end;  // wave-uniform
-  const char* kbase = reinterpret_cast<const char*>(k_idx + row0 * IHD);
+  const char* kbase = reinterpret_cast<const char*>(k_idx + row0 * RB);
 
   // DMA of one tile into buffer b: instruction i, lane l -> tile row
   // r = (i*64 + l) / CPR, LDS slot p = l % CPR, holding global chunk p ^ (r % CPR).
@@ -165,9 +183,24 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       const int c = p ^ (r & (CPR - 1));
       int64_t blk = tile * kTileN + r;
       if (blk > n_vis - 1) blk = n_vis - 1;  // ragged tail: re-read a valid row
-      lds_dma16(kbase + blk * (IHD * 2) + c * 16, &ktile[wave][b][i * 64]);
+      lds_dma16(kbase + blk * RB + c * 16, &ktile[wave][b][i * 64]);
     }
   };
+  // E4M3: the key scales of the wave's blocks (lane col's block of each
+  // tile), loaded before the first tile DMA so that waiting for a tile also
+  // waits for them
+  float ksc[kMaxTpw];
+  if constexpr (F8) {
+#pragma unroll
+    for (int j = 0; j < kMaxTpw; ++j) {
+      ksc[j] = 1.0f;
+      if (j < tiles_per_wave && active) {  // wave-uniform
+        int64_t blk = (tile_begin + j) * kTileN + col;
+        blk = blk < n_vis ? blk : (n_vis > 0 ? n_vis - 1 : 0);
+        ksc[j] = k_scale[row0 + blk];
+      }
+    }
+  }
   if (active) {
     issue_tile(tile_begin, 0);
     if (tile_begin + 1 < tile_end) issue_tile(tile_begin + 1, 1);
@@ -183,7 +216,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       cand_publish(0ull, 0u, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
     return;
   }
-  u32x4 qv[kQRegs ? MT : 1][KS];
+  Op qv[kQRegs ? MT : 1][KS];
   if constexpr (kQRegs) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -204,11 +237,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       const int b = j & 1;
       // all but the next tile's DMA (if issued) have landed
       if (tile + 1 < tile_end) wait_vmcnt<LPT>(); else wait_vmcnt<0>();
-      u32x4 kb[KS];
+      Op kb[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int c = 2 * s + half;
-        kb[s] = ktile[wave][b][col * CPR + (c ^ (col & (CPR - 1)))];
+        if constexpr (F8) {
+          kb[s] = reinterpret_cast<const uint2*>(&ktile[wave][b][0])[(col * CPR + (s ^ (col & (CPR - 1)))) * 2 + half];
+        } else {
+          const int c = 2 * s + half;
+          kb[s] = ktile[wave][b][col * CPR + (c ^ (col & (CPR - 1)))];
+        }
       }
       wait_lgkmcnt0();  // buffer b is free again
       if (tile + 2 < tile_end) issue_tile(tile + 2, b);
@@ -218,12 +255,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, kb[s]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const u32x4 qa = kQRegs ? qv[kQRegs ? mt : 0][s] : q_operand(mt, s);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa), kv,
-                                                            acc[mt], 0, 0, 0);
+          const Op qa = kQRegs ? qv[kQRegs ? mt : 0][s] : q_operand(mt, s);
+          if constexpr (F8)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(
+                __builtin_bit_cast(long, qa), __builtin_bit_cast(long, kb[s]), acc[mt], 0, 0, 0);
+          else
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, kb[s]), acc[mt], 0, 0, 0);
         }
       }
       float part = 0.0f;
@@ -233,6 +273,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
         for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
       }
       part += __shfl_xor(part, 32);
+      if constexpr (F8) part *= ksc[j];
       sc[j] = part;
       if (ca.cand != nullptr) {
         // Merge this tile into the running list (sorted, descending) while
@@ -294,9 +335,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
 template <int IHD, int MT>
 hipError_t launch_t(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t s) {
   dim3 grid(p.wgs_per_token, a.T);
-  hipLaunchKernelGGL((index_score_kernel<IHD, MT>), grid, dim3(kWaves * 64), 0, s, a.q_idx, a.w,
-                     a.k_idx, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.n_ih, a.ratio, a.scores,
-                     a.ld, a.cand, a.err, p.tiles_per_wave);
+  const uint8_t* q = static_cast<const uint8_t*>(a.q_idx);
+  const uint8_t* k = static_cast<const uint8_t*>(a.k_idx);
+  if (a.e4m3)
+    hipLaunchKernelGGL((index_score_kernel<IHD, MT, true>), grid, dim3(kWaves * 64), 0, s, q,
+                       a.q_scale, a.w, k, a.k_scale, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.n_ih,
+                       a.ratio, a.scores, a.ld, a.cand, a.err, p.tiles_per_wave);
+  else
+    hipLaunchKernelGGL((index_score_kernel<IHD, MT, false>), grid, dim3(kWaves * 64), 0, s, q,
+                       nullptr, a.w, k, nullptr, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.n_ih,
+                       a.ratio, a.scores, a.ld, a.cand, a.err, p.tiles_per_wave);
   return hipGetLastError();
 }
 
@@ -309,6 +357,86 @@ hipError_t launch_ihd(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t
     case 4: return launch_t<IHD, 4>(a, p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Rescoring of the E4M3 prefilter's candidates with the bf16 queries and
+// keys.  A wave takes 32 candidates as one MFMA tile: lane (col, half) reads
+// its candidate's key row straight into the B operand registers (16 bytes a
+// k-step) and its query rows from L2, and the score is formed by the same
+// sequence of operations as in the bf16 indexer kernel, so that a candidate's
+// score is the bf16 indexer's score of its block.
+template <int IHD, int MT>
+__global__ __launch_bounds__(256) void rescore_kernel(RescoreLaunch a) {
+  constexpr int KS = IHD / 16;
+  constexpr int RB = 2 * IHD;
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.gcut[t] = 0ull;
+  const int64_t j0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
+  if (j0 >= a.C) return;  // wave-uniform
+  const int64_t j = j0 + col;
+  uint64_t* out = a.key + (int64_t)t * a.C;
+  const int32_t cnt = a.count[t];
+  if (j0 >= cnt) {  // wave-uniform: no candidate in this tile
+    if (half == 0 && j < a.C) out[j] = 0ull;
+    return;
+  }
+  // lanes past the count re-read the last candidate (a valid row)
+  const bool valid = j < cnt;
+  const int32_t b = a.idx[(int64_t)t * a.C + (valid ? j : cnt - 1)];
+  const char* krow = reinterpret_cast<const char*>(a.k_idx) + (a.seq_kv[t] + b) * RB;
+  u32x4 kb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kb[s] = *reinterpret_cast<const u32x4*>(krow + (2 * s + half) * 16);
+  u32x4 qa[MT][KS];
+  float wv[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int hq = mt * 32 + col < a.n_ih ? mt * 32 + col : a.n_ih - 1;
+    const char* qrow = reinterpret_cast<const char*>(a.q_idx) + ((int64_t)t * a.n_ih + hq) * RB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qrow + (2 * s + half) * 16);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      wv[mt][r] = hw < a.n_ih ? a.w[(int64_t)t * a.n_ih + hw] : 0.0f;
+    }
+  }
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[mt][s]),
+                                                        __builtin_bit_cast(bf16x8, kb[s]), acc[mt],
+                                                        0, 0, 0);
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+  }
+  part += __shfl_xor(part, 32);
+  const uint32_t sk = score_key(part);
+  if (half == 0 && j < a.C)
+    out[j] = valid && sk != 0u ? ((uint64_t)sk << 32) | (uint32_t)~(uint32_t)b : 0ull;
+}
+
+template <int IHD>
+hipError_t launch_rescore_ihd(const RescoreLaunch& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.C + 127) / 128), (unsigned)a.T);
+  switch ((a.n_ih + 31) / 32) {
+    case 1: hipLaunchKernelGGL((rescore_kernel<IHD, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((rescore_kernel<IHD, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((rescore_kernel<IHD, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((rescore_kernel<IHD, 4>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -335,6 +463,16 @@ hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s) {
     case 32: return launch_ihd<32>(a, p, s);
     case 64: return launch_ihd<64>(a, p, s);
     case 128: return launch_ihd<128>(a, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_rescore(const RescoreLaunch& a, hipStream_t s) {
+  if (a.T == 0 || a.C == 0) return hipSuccess;
+  switch (a.ihd) {
+    case 32: return launch_rescore_ihd<32>(a, s);
+    case 64: return launch_rescore_ihd<64>(a, s);
+    case 128: return launch_rescore_ihd<128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,7 +17,7 @@ FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced here
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "csa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -27,14 +27,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.EXPORTS)
 
 
 def test_status_strings_and_version(lib):
-    assert b.csa_abi_version() == 1
+    assert b.csa_abi_version() == 2
     assert b.csa_status_str(0) == "CSA_OK"
     for s in (1, 2, 3, 4):
         assert b.csa_status_str(s).startswith("CSA_E")
@@ -46,6 +46,25 @@ def _index(lib, **kw):
              T=1, n_ih=64, ihd=128, ratio=4, scores=FAKE, ld=100, err=None, stream=None)
     a.update(kw)
     return lib.csa_index_score(*a.values())
+
+
+def test_index_score_e4m3_and_quantize_validation(lib):
+    a = dict(q_idx=FAKE, q_scale=FAKE, w=FAKE, k_idx=FAKE, k_scale=FAKE, k_rows=100, pos=FAKE,
+             seq_kv=FAKE, n_comp=FAKE, T=1, n_ih=64, ihd=128, ratio=4, scores=FAKE, ld=100,
+             err=None, stream=None)
+    f = lambda **kw: lib.csa_index_score_e4m3(*dict(a, **kw).values())  # noqa: E731
+    assert f(T=0) == b.CSA_OK
+    assert f(q_scale=None) == b.CSA_EINVAL
+    assert f(k_scale=None) == b.CSA_EINVAL
+    assert f(k_idx=FAKE + 8) == b.CSA_EINVAL                 # codes must be 16-byte aligned
+    assert f(ihd=48) == b.CSA_EUNSUPPORTED
+    q = lambda **kw: lib.csa_quantize_e4m3(*dict(dict(src=FAKE, rows=10, d=128, codes=FAKE,  # noqa: E731
+                                                      scale=FAKE, stream=None), **kw).values())
+    assert q(rows=0) == b.CSA_OK
+    assert q(d=0) == b.CSA_EINVAL
+    assert q(d=513) == b.CSA_EUNSUPPORTED
+    assert q(codes=None) == b.CSA_EINVAL
+    assert q(rows=-1) == b.CSA_EINVAL
 
 
 def test_index_score_validation(lib):
@@ -137,6 +156,22 @@ def test_decode_step_validation(lib):
     a.all_kv = None
     assert b.csa_decode_step_workspace_bytes(a) == need
     a.all_kv = FAKE
+    a.idx_e4m3 = 1                # the E4M3 prefilter needs the codes and both scale arrays
+    assert st(FAKE, need) == b.CSA_EINVAL
+    a.q_idx_scale = a.k_idx_scale = FAKE
+    assert st(FAKE, need) == b.CSA_EINVAL
+    a.q_idx8 = a.k_idx8 = FAKE
+    need8 = b.csa_decode_step_workspace_bytes(a)
+    # prefilter of C = 1536 candidates: indices, count, keys and a bound per token
+    assert need8 > need
+    assert need8 - need >= 1536 * 12
+    assert st(FAKE, need) == b.CSA_EWORKSPACE
+    a.k_idx8 = FAKE + 8           # codes are read 16 bytes at a time
+    assert st(FAKE, need8) == b.CSA_EINVAL
+    a.k_idx8 = FAKE
+    a.idx_e4m3 = 2
+    assert st(FAKE, need8) == b.CSA_EINVAL
+    a.idx_e4m3 = 0
     a.head_dim = 100
     assert st(FAKE, need) == b.CSA_EUNSUPPORTED
     a.head_dim = 512
