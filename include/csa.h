@@ -45,7 +45,9 @@ typedef enum csa_status {
   CSA_EINVAL = 1,        /* null required pointer, negative size, bad value   */
   CSA_EUNSUPPORTED = 2,  /* shape outside the compiled set (see each call)    */
   CSA_EWORKSPACE = 3,    /* ws NULL, misaligned (256 B) or smaller than needed */
-  CSA_EHIP = 4           /* the HIP runtime rejected a launch                  */
+  CSA_EHIP = 4,          /* the HIP runtime rejected a launch                  */
+  CSA_ESCRATCH = 5       /* csa_decode_step_noalloc: workspace need above
+                            CSA_NOALLOC_SCRATCH_BYTES                          */
 } csa_status;
 
 /* Device-side error bits ORed into *err. */
@@ -252,6 +254,26 @@ typedef struct csa_step_args {
 
 size_t csa_decode_step_workspace_bytes(const csa_step_args* a);
 csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free decode step, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, computation and results as
+ * csa_decode_step; its workspace is a fixed array of
+ * CSA_NOALLOC_SCRATCH_BYTES (64 MiB) in the memory of each GPU the library
+ * runs on, held until the process ends.  The call itself allocates nothing.
+ *   Runs on the current device; `stream` must belong to it (NULL: its null
+ *     stream).  The first call on a device looks the array's address up.
+ *   Returns CSA_ESCRATCH, before any launch, when
+ *     csa_decode_step_workspace_bytes(a) exceeds the array (the 1M-token and
+ *     32 x 16K..128K decode steps need about 2 and 42 MiB).
+ *   Every call on one GPU uses that GPU's one array: calls that may overlap
+ *     in time on one GPU (other streams, other host threads) race and must be
+ *     serialised by the caller.  Each step writes every workspace word it
+ *     reads before reading it, so nothing needs clearing between calls.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+csa_status csa_decode_step_noalloc(const csa_step_args* a, void* stream);
 
 #ifdef __cplusplus
 }

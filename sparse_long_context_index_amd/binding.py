@@ -20,7 +20,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 _lib = None
 
-CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EWORKSPACE, CSA_EHIP = range(5)
+CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EWORKSPACE, CSA_EHIP, CSA_ESCRATCH = range(6)
+CSA_NOALLOC_SCRATCH_BYTES = 64 << 20
 CSA_MODE_CSA, CSA_MODE_HCA = 0, 1
 DERR = {0x1: "VIS_OVER_LD", 0x2: "KEY_RANGE", 0x4: "BAD_META", 0x8: "ROW_RANGE",
         0x10: "COUNT_RANGE", 0x20: "ROWS_OVER_MAX"}
@@ -67,6 +68,7 @@ _SIGS = {
                               _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp, _vp]),
     "csa_decode_step_workspace_bytes": (_sz, [ctypes.POINTER(StepArgs)]),
     "csa_decode_step": (_i32, [ctypes.POINTER(StepArgs), _vp, _sz, _vp]),
+    "csa_decode_step_noalloc": (_i32, [ctypes.POINTER(StepArgs), _vp]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -216,6 +218,12 @@ def csa_decode_step(args: StepArgs, ws, stream=None):
     _check("csa_decode_step", load().csa_decode_step(
         ctypes.byref(args), _p(ws, (torch.uint8,), "ws", True), 0 if ws is None else ws.numel(),
         _stream(stream)))
+
+
+def csa_decode_step_noalloc(args: StepArgs, stream=None):
+    """csa_decode_step with the library's fixed per-GPU scratch as workspace."""
+    _check("csa_decode_step_noalloc",
+           load().csa_decode_step_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -3,6 +3,8 @@
 // in this file allocates, frees or synchronises.
 #include <math.h>
 
+#include <mutex>
+
 #include "csa_common.h"
 
 using namespace csa;
@@ -19,6 +21,33 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
 csa_status hip_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_EHIP; }
+
+// Workspace of the allocation-free decode step: one array in each GPU's
+// memory, created when the library's code object is loaded on that GPU and
+// held until the process ends.  Host code reaches it only through the device
+// address hipGetSymbolAddress gives on each device (the array's name is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The scratch array's address on the current device, looked up once per
+// device with that device current.
+csa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return CSA_EHIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return CSA_OK;
+}
 
 csa_status check_index(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                        int64_t k_rows, const int64_t* pos, const int64_t* seq_kv,
@@ -174,6 +203,9 @@ const char* csa_status_str(int status) {
     case CSA_EUNSUPPORTED: return "CSA_EUNSUPPORTED: shape outside the supported set";
     case CSA_EWORKSPACE: return "CSA_EWORKSPACE: workspace missing, misaligned or too small";
     case CSA_EHIP: return "CSA_EHIP: HIP launch failed";
+    case CSA_ESCRATCH:
+      return "CSA_ESCRATCH: the step needs more workspace than the allocation-free entry "
+             "point's fixed scratch (CSA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown csa_status";
   }
 }
@@ -384,6 +416,17 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   e = launch_step_select(S, a->T, st);
   if (e == hipSuccess) e = launch_attend(L, st);
   return hip_status(e);
+}
+
+csa_status csa_decode_step_noalloc(const csa_step_args* a, void* stream) {
+  csa_status s = check_step(a);
+  if (s != CSA_OK) return s;
+  if (a->T == 0) return CSA_OK;
+  if (step_ws_layout(a).total > (size_t)CSA_NOALLOC_SCRATCH_BYTES) return CSA_ESCRATCH;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != CSA_OK) return s;
+  return csa_decode_step(a, ws, (size_t)CSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.EXPORTS)
@@ -175,8 +175,16 @@ def test_decode_step_validation(lib):
     a.head_dim = 100
     assert st(FAKE, need) == b.CSA_EUNSUPPORTED
     a.head_dim = 512
+    # the allocation-free step refuses, before touching a GPU, a step whose
+    # workspace would not fit its fixed scratch (here 1 GiB of scores)
+    a.max_vis = 1 << 28
+    assert b.csa_decode_step_workspace_bytes(a) > b.CSA_NOALLOC_SCRATCH_BYTES
+    assert lib.csa_decode_step_noalloc(ctypes.byref(a), None) == b.CSA_ESCRATCH
+    assert "CSA_NOALLOC_SCRATCH_BYTES" in b.csa_status_str(b.CSA_ESCRATCH)
+    a.max_vis = 262144
     a.T = 0
     assert st(FAKE, need) == b.CSA_OK
+    assert lib.csa_decode_step_noalloc(ctypes.byref(a), None) == b.CSA_OK
     assert lib.csa_decode_step(None, FAKE, need, None) == b.CSA_EINVAL
 
 
