@@ -7,16 +7,28 @@ in HBM.  Steps rotate over 30 layer-sized caches (the 30 CSA layers of the
 1M-context sizing: 1.9 GiB of indexer keys, 7.5 GiB of compressed KV) so that
 every step streams its keys from HBM rather than from the 256 MB last-level
 cache.  Timed steps are replayed from HIP graphs, bracketed by device
-synchronisation.
+synchronisation; each replay is also timed on its own, for the median and the
+10th / 90th percentiles of the per-step time.
 
 Also reported:
-  roofline     -- the dominant kernel (indexer scoring): its algorithmic bytes
-                  per launch over its mean launch duration measured here with
-                  HIP events on its stream, against 8 TB/s;
-  cpu_baseline -- the fp64 numpy oracle timed on a bounded sample of the same
-                  workload on this host's cores (a reported baseline only).
+  roofline     -- the dominant kernel, the step's own indexer launch (scores
+                  and candidate lists, csa_decode_step_stage INDEX): its
+                  algorithmic bytes over its mean launch duration, measured
+                  here with HIP events on its stream, against 8 TB/s; its HBM
+                  traffic from the committed rocprofv3 counter summary when
+                  that was taken on the current kernel source;
+  stages       -- the same for the rest of the step (select, attention,
+                  combine);
+  configs      -- the other workloads, each from repeated graph replays:
+                  the dense HCA step at 1M, the 32K step, a batch of 32
+                  sequences of 16K..128K tokens, a 4096-token prefill chunk
+                  (indexer as a fraction of bf16 MFMA peak) and the 1M step
+                  with E4M3 indexer keys;
+  cpu_baseline -- the fp64 numpy oracle timed on a bounded sample of the
+                  headline workload on this host's cores (a reported baseline
+                  only).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
 """
 from __future__ import annotations
 
@@ -32,39 +44,50 @@ sys.path.insert(0, ROOT)
 
 LAYERS = 30
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "CSA decode steps/sec per layer at 1M ctx; achieved HBM GB/s vs peak"
+SRC_FILES = ("index_score.hip", "csa_common.h")
 
 
-def _kernel_src_hash() -> str:
+def kernel_src_hash(files=SRC_FILES) -> str:
     h = hashlib.sha256()
-    for f in ("index_score.hip", "csa_common.h"):
+    for f in files:
         with open(os.path.join(ROOT, "sparse_long_context_index_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def _traffic_per_launch():
-    """HBM bytes per indexer launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "index_score_1m_counters.json")
+    """HBM bytes per in-step indexer launch from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "decode_step_1m_counters.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_src_sha256_16") != _kernel_src_hash():
+    k = d.get("kernels", {}).get("index_score", {})
+    if k.get("src_sha256_16") != kernel_src_hash(tuple(k.get("src_files", SRC_FILES))):
         return None
-    return d.get("hbm_bytes_per_launch")
+    return k.get("hbm_bytes_per_launch")
+
+
+def _cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return max(1, min(blas, avail))
 
 
 def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
     """Time the oracle (unchanged) on whole 1M steps until ~budget_s."""
-    import numpy as np
     from oracle import csa_token
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _cpu_threads()
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -75,7 +98,83 @@ def cpu_baseline(inp, budget_s: float = 12.0) -> dict:
             break
     return {"value": n / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} full 1M-context CSA decode steps (token 0, layer 0), "
-                      f"{el:.1f} s, numpy fp64, BLAS threads={threads}"}
+                      f"{el:.1f} s, numpy fp64, {threads} BLAS threads"}
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def _dist_us(per_step_ms):
+    return {"median": round(_pct(per_step_ms, 0.5) * 1e3, 3),
+            "p10": round(_pct(per_step_ms, 0.1) * 1e3, 3),
+            "p90": round(_pct(per_step_ms, 0.9) * 1e3, 3)}
+
+
+class Runner:
+    """Graph capture and event timing of library calls on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def capture(self, calls):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for c in calls:
+                c()
+        return g
+
+    def replays(self, g, n_calls, replays, warm=2):
+        """Per-call ms of each of `replays` replays of g (n_calls calls each)."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for _ in range(warm):
+                g.replay()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(replays)]
+            for e0, e1 in evs:
+                e0.record(self.stream)
+                g.replay()
+                e1.record(self.stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) / n_calls for e0, e1 in evs]
+
+
+def step_bytes(inp, t_list=None):
+    """Minimum HBM bytes of a CSA step: the visible indexer keys, the indexer
+    queries and weights, the selected and SWA rows, attention q and output."""
+    total = 0
+    for t in (range(inp.T) if t_list is None else t_list):
+        n = min(int(inp.pos[t]) // inp.ratio, int(inp.n_comp[t]))
+        k = min(inp.top_k, n)
+        sw = int(inp.swa_len[t])
+        total += (n * inp.ihd * 2 + inp.n_ih * inp.ihd * 2 + inp.n_ih * 4
+                  + (k + sw) * inp.head_dim * 2 + 2 * inp.n_heads * inp.head_dim * 2)
+    return total
+
+
+def index_bytes(inp, n_lists_words, e4m3=False):
+    """Algorithmic bytes of one indexer launch of the step: keys (and their
+    scales), queries, weights, one fp32 score per visible block and the
+    candidate lists written."""
+    total = n_lists_words * 8
+    for t in range(inp.T):
+        n = min(int(inp.pos[t]) // inp.ratio, int(inp.n_comp[t]))
+        kb = inp.ihd + 4 if e4m3 else inp.ihd * 2
+        qb = inp.n_ih * (inp.ihd + 4) if e4m3 else inp.n_ih * inp.ihd * 2
+        total += n * kb + qb + inp.n_ih * 4 + n * 4
+    return total
+
+
+def lists_words(T, n_vis):
+    """Candidate-list words (keys + group bounds) the step's indexer writes
+    for T tokens of n_vis blocks: one list of 16 keys per 1024-block group
+    (the merged plan of the long rows benchmarked here)."""
+    groups = (n_vis + 1023) // 1024
+    return T * groups * 17
 
 
 def main() -> int:
@@ -84,56 +183,67 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-configs", action="store_true", help="headline workload only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "sharding the path over several GPUs is not built", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     from sparse_long_context_index_amd import binding as B
     from sparse_long_context_index_amd import inputs as gen
 
+    def log(msg):
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
+
     dev = torch.device("cuda:0")
     B.load()
-    print("bench: generating the 1M-context workload", file=sys.stderr, flush=True)
-    inp = gen.ctx1m()
-    d0 = B.upload(inp, dev)
-    layers = [d0]
-    for _ in range(LAYERS - 1):
-        dl = dict(d0)
-        dl["k_idx"] = d0["k_idx"].clone()
-        dl["comp_kv"] = d0["comp_kv"].clone()
-        layers.append(dl)
-    outs = B.alloc_step_outputs(inp, dev, keep=False, all_kv=False)
-    step_args = [B.step_args(inp, dl, outs) for dl in layers]
-    ws = B.step_workspace(step_args[0], dev)
-    torch.cuda.synchronize()
-    print("bench: warmup", file=sys.stderr, flush=True)
-
     stream = torch.cuda.Stream()
+    R = Runner(torch, stream)
+
+    def check_err(outs, what):
+        torch.cuda.synchronize()
+        e = int(outs["err"].item())
+        if e != 0:
+            raise RuntimeError(f"{what}: device error word {e:#x}")
+
+    def layered(inp, n_layers, e4m3=False):
+        """Device copies of the batch with n_layers private key/KV caches."""
+        d0 = B.upload(inp, dev)
+        if e4m3:
+            d0 = B.quantize_indexer_e4m3(d0)
+        layers = [d0]
+        for _ in range(n_layers - 1):
+            dl = dict(d0)
+            for k in ("k_idx", "comp_kv") + (("k_idx8", "k_scale") if e4m3 else ()):
+                dl[k] = d0[k].clone()
+            layers.append(dl)
+        return layers
+
+    # ---------------- headline: 1M-context CSA decode step ----------------
+    log("generating the 1M-context workload")
+    inp = gen.ctx1m()
+    layers = layered(inp, LAYERS)
+    outs = B.alloc_step_outputs(inp, dev, keep=False, all_kv=False)
+    sargs = [B.step_args(inp, dl, outs) for dl in layers]
+    ws = B.step_workspace(sargs[0], dev)
+    torch.cuda.synchronize()
+    log("warmup")
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            B.csa_decode_step(step_args[i % LAYERS], ws)
-    torch.cuda.synchronize()
-    if int(outs["err"].item()) != 0:
-        raise RuntimeError(f"device error word {int(outs['err'].item()):#x}")
+            B.csa_decode_step(sargs[i % LAYERS], ws)
+    check_err(outs, "1M step warmup")
 
-    # Graphs: one replay = LAYERS consecutive steps (+ a remainder graph).
-    def capture(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(n):
-                B.csa_decode_step(step_args[i % LAYERS], ws)
-        return g
-    g_full = capture(LAYERS)
+    step_call = lambda i: (lambda: B.csa_decode_step(sargs[i % LAYERS], ws))  # noqa: E731
+    g_full = R.capture([step_call(i) for i in range(LAYERS)])
     rem = args.steps % LAYERS
-    g_rem = capture(rem) if rem else None
+    g_rem = R.capture([step_call(i) for i in range(rem)]) if rem else None
     torch.cuda.synchronize()
 
-    print("bench: timed steps", file=sys.stderr, flush=True)
+    log("timed steps")
+    n_full = args.steps // LAYERS
     with torch.cuda.stream(stream):
         for _ in range(2):
             g_full.replay()
@@ -141,9 +251,13 @@ def main() -> int:
         t0 = time.perf_counter()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
+        rep_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n_full)]
         ev0.record(stream)
-        for _ in range(args.steps // LAYERS):
+        for e0, e1 in rep_ev:
+            e0.record(stream)
             g_full.replay()
+            e1.record(stream)
         if g_rem is not None:
             g_rem.replay()
         ev1.record(stream)
@@ -152,42 +266,26 @@ def main() -> int:
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
     steps_per_s = args.steps / (gpu_ms / 1e3)
-    if int(outs["err"].item()) != 0:
-        raise RuntimeError(f"device error word {int(outs['err'].item()):#x}")
+    step_dist = _dist_us([e0.elapsed_time(e1) / LAYERS for e0, e1 in rep_ev]) if rep_ev else None
+    check_err(outs, "1M timed steps")
 
-    # Dominant kernel: indexer scoring, launched through csa_index_score on
-    # `stream` back to back over the rotated layers (as the kernels of the
-    # step run), between two HIP events recorded on that stream.
-    print("bench: indexer kernel timing", file=sys.stderr, flush=True)
+    # ---------------- the step's stages on their own ----------------
+    log("stage timing (the step's indexer launch; the rest)")
+    stage = lambda i, k: (lambda: B.csa_decode_step_stage(sargs[i % LAYERS], k, ws))  # noqa: E731
+    g_idx = R.capture([stage(i, B.CSA_STAGE_INDEX) for i in range(LAYERS)])
+    idx_ms = R.replays(g_idx, LAYERS, 16)
+    # the rest reads what one indexer stage left in the workspace
+    g_rest = R.capture([stage(i, B.CSA_STAGE_REST) for i in range(LAYERS)])
+    rest_ms = R.replays(g_rest, LAYERS, 16)
+    check_err(outs, "stages")
+    k_ms = sum(idx_ms) / len(idx_ms)
     n_vis = inp.max_visible()
-    scores = torch.empty((1, n_vis), dtype=torch.float32, device=dev)
-    reps = LAYERS * 8
-
-    def index_launch(i):
-        dl = layers[i % LAYERS]
-        B.csa_index_score(dl["q_idx"], dl["w"], dl["k_idx"], dl["pos"], dl["seq_kv"],
-                          dl["n_comp"], inp.n_ih, inp.ihd, inp.ratio, scores, n_vis)
-
-    with torch.cuda.stream(stream):
-        for i in range(LAYERS):
-            index_launch(i)
-        k0 = torch.cuda.Event(enable_timing=True)
-        k1 = torch.cuda.Event(enable_timing=True)
-        k0.record(stream)
-        for i in range(reps):
-            index_launch(i)
-        k1.record(stream)
-    torch.cuda.synchronize()
-    k_ms = k0.elapsed_time(k1) / reps
-    # algorithmic bytes of one indexer launch: keys + queries + weights read,
-    # one fp32 score per visible block written
-    idx_bytes = n_vis * inp.ihd * 2 + inp.n_ih * inp.ihd * 2 + inp.n_ih * 4 + n_vis * 4
+    idx_bytes = index_bytes(inp, lists_words(1, n_vis))
     achieved = idx_bytes / (k_ms * 1e-3) / 1e9
     traffic = _traffic_per_launch()
 
-    # Secondary denominator: a plain device copy of 1 GiB on the same stream
-    # (its rocprofv3 FETCH_SIZE / WRITE_SIZE also calibrate the counters).
-    print("bench: device copy bandwidth", file=sys.stderr, flush=True)
+    # ---------------- device copy (secondary denominator) ----------------
+    log("device copy bandwidth")
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     with torch.cuda.stream(stream):
@@ -202,16 +300,18 @@ def main() -> int:
     copy_gbs = 10 * 2 * csrc.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc, cdst
 
-    # minimum bytes of a whole step (keys, indexer q and w, selected rows, SWA
-    # rows, attention q, output)
-    step_bytes = (n_vis * inp.ihd * 2 + inp.n_ih * inp.ihd * 2 + inp.n_ih * 4
-                  + inp.top_k * inp.head_dim * 2 + inp.window * inp.head_dim * 2
-                  + 2 * inp.n_heads * inp.head_dim * 2)
-    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    sb = step_bytes(inp)
+    step_gbs = sb / (ms_per_step * 1e-3) / 1e9
+
+    configs = {}
+    if not args.no_configs:
+        configs = other_configs(torch, B, gen, R, dev, stream, layered, check_err, log)
+    del layers, sargs, ws
+    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
-        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        log("CPU oracle baseline")
         cpu = cpu_baseline(inp)
 
     line = {
@@ -230,19 +330,141 @@ def main() -> int:
         "config": {"workload": "1M-context CSA decode step, one layer: 262,144 blocks, "
                                "n_ih 64 x ihd 128, top_k 1024, window 128, 64 heads x 512",
                    "layers_rotated": LAYERS, "batch": 1, "context_tokens": 1 << 20},
-        "step_min_bytes": step_bytes,
+        "step_us": step_dist,
+        "step_min_bytes": sb,
         "step_effective_gbs": round(step_gbs, 1),
         "step_roofline_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "index_score_kernel<128,2>",
+        "roofline": {"bound": "hbm", "kernel": "index_score_kernel<128,2,false> (the step's "
+                                               "launch, with candidate lists)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": idx_bytes, "mean_launch_us": round(k_ms * 1e3, 3)},
+                     "bytes_per_launch": idx_bytes, "mean_launch_us": round(k_ms * 1e3, 3),
+                     "launch_us": _dist_us(idx_ms), "src_sha256_16": kernel_src_hash()},
+        "stages": {"index_us": _dist_us(idx_ms), "rest_us": _dist_us(rest_ms)},
         "device_copy_gbs": round(copy_gbs, 1),
+        "configs": configs,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line))
     return 0
+
+
+def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dict:
+    """The other workloads, each as graph replays of rotated layers."""
+    res = {}
+
+    def csa_config(name, inp, n_layers, replays, e4m3=False, index_stage=False):
+        layers = layered(inp, n_layers, e4m3=e4m3)
+        outs = B.alloc_step_outputs(inp, dev, keep=False, all_kv=False)
+        sargs = [B.step_args(inp, dl, outs, e4m3=e4m3) for dl in layers]
+        ws = B.step_workspace(sargs[0], dev)
+        g = R.capture([(lambda a=a: B.csa_decode_step(a, ws)) for a in sargs])
+        ms = R.replays(g, n_layers, replays)
+        check_err(outs, name)
+        r = {"step_us": _dist_us(ms)}
+        if index_stage:
+            gi = R.capture([(lambda a=a: B.csa_decode_step_stage(a, B.CSA_STAGE_INDEX, ws))
+                            for a in sargs])
+            r["index_us"] = _dist_us(R.replays(gi, n_layers, replays))
+            check_err(outs, name + " index stage")
+        del layers, sargs, ws, g
+        torch.cuda.empty_cache()
+        return r
+
+    # E4M3 indexer keys at 1M
+    log("config: 1M step with E4M3 indexer keys")
+    inp = gen.ctx1m()
+    r = csa_config("e4m3_1m", inp, LAYERS, 20, e4m3=True, index_stage=True)
+    ib = index_bytes(inp, lists_words(1, inp.max_visible()), e4m3=True)
+    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+    r["index_gbs"] = round(ib / (r["index_us"]["median"] * 1e-6) / 1e9, 1)
+    r["index_frac"] = round(r["index_gbs"] / HBM_PEAK_GBS, 4)
+    r["index_bytes"] = ib
+    r["workload"] = ("1M-context CSA decode step with E4M3 indexer keys and queries "
+                     "(prefilter of 1536, bf16 rescore)")
+    res["e4m3_1m"] = r
+
+    # 32K context
+    log("config: 32K-context step")
+    inp = gen.ctx32k()
+    r = csa_config("ctx_32k", inp, LAYERS, 20)
+    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+    r["workload"] = "32K-context CSA decode step: 8192 blocks, batch 1"
+    res["ctx_32k"] = r
+
+    # batch of 32 sequences
+    log("config: batch of 32 sequences")
+    inp = gen.batched()
+    r = csa_config("batched_32", inp, 4, 20)
+    sb = step_bytes(inp)
+    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+    r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
+    r["min_bytes"] = sb
+    r["gbs"] = round(sb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
+    r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    r["workload"] = "32 sequences, lengths uniform in [16K, 128K], one decode token each"
+    res["batched_32"] = r
+
+    # 4096-token prefill chunk
+    log("config: 4096-token prefill chunk")
+    inp = gen.prefill()
+    r = csa_config("prefill_4096", inp, 1, 5, index_stage=True)
+    flops = 0
+    for t in range(inp.T):
+        n = min(int(inp.pos[t]) // inp.ratio, int(inp.n_comp[t]))
+        flops += 2 * n * inp.n_ih * inp.ihd
+    r["index_tflops"] = round(flops / (r["index_us"]["median"] * 1e-6) / 1e12, 1)
+    r["index_frac_bf16_mfma"] = round(r["index_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    r["index_flops"] = flops
+    r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
+    r["workload"] = "prefill chunk: 4096 query tokens at positions 61440..65535, 16384 blocks"
+    res["prefill_4096"] = r
+
+    # dense HCA at 1M
+    log("config: dense HCA step at 1M")
+    h = gen.hca1m()
+    nl = 60  # 60 x 8.5 MB of rows: well past the last-level cache
+
+    def tdev(a, dt):
+        return torch.as_tensor(a).to(dev) if dt is None else torch.as_tensor(a, dtype=dt).to(dev)
+
+    bf = lambda a: torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)  # noqa: E731
+    base = {"q": bf(h.q), "swa": bf(h.swa), "pos": tdev(h.pos, torch.int64),
+            "seq_kv": tdev(h.seq_kv, torch.int64), "n_comp": tdev(h.n_comp, torch.int32),
+            "swa_row0": tdev(h.swa_row0, torch.int64), "swa_len": tdev(h.swa_len, torch.int32)}
+    kv0 = bf(h.comp_kv)
+    kvs = [kv0] + [kv0.clone() for _ in range(nl - 1)]
+    out = torch.zeros((h.T, h.n_heads, h.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((h.T, h.n_heads), dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    hargs = []
+    for kv in kvs:
+        a = B.StepArgs()
+        a.mode, a.T, a.ratio, a.window = B.CSA_MODE_HCA, h.T, h.ratio, 128
+        a.n_heads, a.head_dim, a.max_vis, a.scale = h.n_heads, h.head_dim, 8192, h.scale
+        for k, v in base.items():
+            setattr(a, k, v.data_ptr())
+        a.comp_kv, a.comp_rows, a.swa_rows = kv.data_ptr(), h.comp_kv.shape[0], h.swa.shape[0]
+        a.out, a.lse, a.err = out.data_ptr(), lse.data_ptr(), err.data_ptr()
+        hargs.append(a)
+    hws = B.step_workspace(hargs[0], dev)
+    g = R.capture([(lambda a=a: B.csa_decode_step(a, hws)) for a in hargs])
+    ms = R.replays(g, nl, 20)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"hca_1m: device error word {int(err.item()):#x}")
+    rows = 8192 + 128
+    hb = rows * h.head_dim * 2 + 2 * h.n_heads * h.head_dim * 2
+    r = {"step_us": _dist_us(ms), "min_bytes": hb}
+    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+    r["gbs"] = round(hb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
+    r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+    r["workload"] = "dense HCA decode step at 1M: 8192 ratio-128 blocks + 128 SWA rows, 64 x 512"
+    res["hca_1m"] = r
+    del kvs, hargs, hws, g
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

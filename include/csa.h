@@ -256,6 +256,21 @@ size_t csa_decode_step_workspace_bytes(const csa_step_args* a);
 csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One stage of csa_decode_step, for callers that schedule other work between
+ * the indexer and the rest of the step, or time the stages apart.
+ *   stage CSA_STAGE_INDEX: S1 -- the indexer scores and the candidate lists
+ *     of the top-k, left in ws (and in `scores` when given);
+ *   stage CSA_STAGE_REST: S2 .. S4, reading them from the same ws.
+ * The two in this order on one stream, with the same arguments and ws,
+ * compute exactly what csa_decode_step computes.  In HCA mode the INDEX stage
+ * does nothing.  Same validation and workspace size as csa_decode_step; any
+ * other stage value gives CSA_EINVAL.
+ */
+enum { CSA_STAGE_INDEX = 1, CSA_STAGE_REST = 2 };
+csa_status csa_decode_step_stage(const csa_step_args* a, int stage, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * Allocation-free decode step, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, computation and results as

@@ -22,6 +22,7 @@ _lib = None
 
 CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EWORKSPACE, CSA_EHIP, CSA_ESCRATCH = range(6)
 CSA_NOALLOC_SCRATCH_BYTES = 64 << 20
+CSA_STAGE_INDEX, CSA_STAGE_REST = 1, 2
 CSA_MODE_CSA, CSA_MODE_HCA = 0, 1
 DERR = {0x1: "VIS_OVER_LD", 0x2: "KEY_RANGE", 0x4: "BAD_META", 0x8: "ROW_RANGE",
         0x10: "COUNT_RANGE", 0x20: "ROWS_OVER_MAX"}
@@ -69,6 +70,7 @@ _SIGS = {
     "csa_decode_step_workspace_bytes": (_sz, [ctypes.POINTER(StepArgs)]),
     "csa_decode_step": (_i32, [ctypes.POINTER(StepArgs), _vp, _sz, _vp]),
     "csa_decode_step_noalloc": (_i32, [ctypes.POINTER(StepArgs), _vp]),
+    "csa_decode_step_stage": (_i32, [ctypes.POINTER(StepArgs), _i32, _vp, _sz, _vp]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -218,6 +220,12 @@ def csa_decode_step(args: StepArgs, ws, stream=None):
     _check("csa_decode_step", load().csa_decode_step(
         ctypes.byref(args), _p(ws, (torch.uint8,), "ws", True), 0 if ws is None else ws.numel(),
         _stream(stream)))
+
+
+def csa_decode_step_stage(args: StepArgs, stage: int, ws, stream=None):
+    _check("csa_decode_step_stage", load().csa_decode_step_stage(
+        ctypes.byref(args), int(stage), _p(ws, (torch.uint8,), "ws", True),
+        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def csa_decode_step_noalloc(args: StepArgs, stream=None):

@@ -326,7 +326,15 @@ size_t csa_decode_step_workspace_bytes(const csa_step_args* a) {
   return step_ws_layout(a).total;
 }
 
-csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step's stages: kStageIndex (S1 and its candidate lists) and
+// kStageRest (S2 .. S4, reading what S1 left in the workspace).
+constexpr int kStageIndex = 1, kStageRest = 2;
+
+csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream, int stages) {
   csa_status s = check_step(a);
   if (s != CSA_OK) return s;
   if (a->T == 0) return CSA_OK;
@@ -342,6 +350,7 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   L.ws = base + lay.attend; L.err = a->err;
 
   if (a->mode == CSA_MODE_HCA) {
+    if (!(stages & kStageRest)) return CSA_OK;
     L.kv_a = a->comp_kv; L.a_rows = a->comp_rows; L.a_row0 = a->seq_kv; L.a_len = nullptr;
     L.a_stride = 0; L.vis_pos = a->pos; L.vis_ncomp = a->n_comp; L.vis_ratio = a->ratio;
     L.kv_b = a->swa; L.b_rows = a->swa_rows; L.b_row0 = a->swa_row0; L.b_len = a->swa_len;
@@ -370,8 +379,12 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   I.T = a->T; I.n_ih = a->n_ih; I.ihd = a->ihd; I.ratio = a->ratio;
   I.scores = scores; I.ld = a->max_vis;
   I.cand = cand_args(tp, tw); I.err = a->err;
-  hipError_t e = launch_index_score(I, st);
-  if (e != hipSuccess) return hip_status(e);
+  hipError_t e = hipSuccess;
+  if (stages & kStageIndex) {
+    e = launch_index_score(I, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!(stages & kStageRest)) return CSA_OK;
   // S2, then S3 fused into S4: the selected compressed rows are read through
   // their block indices and the SWA rows in place (and copied into all_kv
   // when it is given)
@@ -416,6 +429,20 @@ csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, vo
   e = launch_step_select(S, a->T, st);
   if (e == hipSuccess) e = launch_attend(L, st);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return run_step(a, ws, ws_bytes, stream, kStageIndex | kStageRest);
+}
+
+csa_status csa_decode_step_stage(const csa_step_args* a, int stage, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (stage != CSA_STAGE_INDEX && stage != CSA_STAGE_REST) return CSA_EINVAL;
+  return run_step(a, ws, ws_bytes, stream, stage == CSA_STAGE_INDEX ? kStageIndex : kStageRest);
 }
 
 csa_status csa_decode_step_noalloc(const csa_step_args* a, void* stream) {

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.EXPORTS)
@@ -182,6 +182,10 @@ def test_decode_step_validation(lib):
     assert lib.csa_decode_step_noalloc(ctypes.byref(a), None) == b.CSA_ESCRATCH
     assert "CSA_NOALLOC_SCRATCH_BYTES" in b.csa_status_str(b.CSA_ESCRATCH)
     a.max_vis = 262144
+    stage = lambda k, ws, n: lib.csa_decode_step_stage(ctypes.byref(a), k, ws, n, None)  # noqa: E731
+    assert stage(0, FAKE, need) == b.CSA_EINVAL and stage(3, FAKE, need) == b.CSA_EINVAL
+    assert stage(b.CSA_STAGE_INDEX, FAKE, need - 1) == b.CSA_EWORKSPACE
+    assert stage(b.CSA_STAGE_REST, None, 0) == b.CSA_EWORKSPACE
     a.T = 0
     assert st(FAKE, need) == b.CSA_OK
     assert lib.csa_decode_step_noalloc(ctypes.byref(a), None) == b.CSA_OK

@@ -321,6 +321,34 @@ def test_decode_step_1m_deterministic(dev):
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("e4m3", [False, True])
+def test_decode_step_stages_equal_whole_step(dev, e4m3):
+    say(f"csa_decode_step_stage INDEX then REST == csa_decode_step (1M, e4m3={e4m3})")
+    inp = gen.ctx1m()
+    b = B()
+    d = b.upload(inp, dev)
+    if e4m3:
+        d = b.quantize_indexer_e4m3(d)
+    res = []
+    for staged in (False, True):
+        outs = b.alloc_step_outputs(inp, dev)
+        a = b.step_args(inp, d, outs, e4m3=e4m3)
+        ws = b.step_workspace(a, dev)
+        if staged:
+            b.csa_decode_step_stage(a, b.CSA_STAGE_INDEX, ws)
+            b.csa_decode_step_stage(a, b.CSA_STAGE_REST, ws)
+        else:
+            b.csa_decode_step(a, ws)
+        torch.cuda.synchronize()
+        res.append({k: v.cpu() for k, v in outs.items()})
+    for k in res[0]:
+        x, y = res[0][k], res[1][k]
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), k
+    assert int(res[0]["err"][0]) == 0
+
+
 def test_decode_step_batched(dev):
     say("csa_decode_step batched: 32 sequences of 16K..128K tokens")
     inp = gen.batched()
