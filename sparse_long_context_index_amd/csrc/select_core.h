@@ -766,100 +766,148 @@ __device__ __forceinline__ bool fast_select(const uint64_t (&key)[KP], const uin
     sh.wmax[wave] = hi;
   }
   __syncthreads();
-  const uint32_t blo = wave_min_u32(lane < W ? sh.wmin[lane] : 0xFFFFFFFFu);
-  const uint32_t bhi = wave_max_u32(lane < W ? sh.wmax[lane] : 0u);
-  const uint32_t range = bhi - blo;
-  if (bhi == 0u || range == 0u) {  // no keys, or a single score value
+  // The keys still in play have score words in [blo, bhi]; kk of them are
+  // at or above the threshold.  A pass bins them linearly over that range;
+  // when the threshold bin is crowded (a few far outliers stretch the range)
+  // the next pass re-bins that bin's keys alone, over their own range.
+  uint32_t blo = wave_min_u32(lane < W ? sh.wmin[lane] : 0xFFFFFFFFu);
+  uint32_t bhi = wave_max_u32(lane < W ? sh.wmax[lane] : 0u);
+  if (bhi == 0u || bhi == blo) {  // no keys, or a single score value
     __syncthreads();
     return false;
   }
-  const bool small = range < (uint32_t)kFastBins;
-  const uint32_t mul =
-      small ? 0u : (uint32_t)((float)kFastBins * 4294967296.0f / ((float)range + 1.0f) * 0.99999f);
+  uint32_t kk = k;
+  bool small = false;
+  uint32_t mul = 0u;
+  auto in_play = [&](uint64_t c) {
+    const uint32_t h = (uint32_t)(c >> 32);
+    return c != 0ull && h >= blo && h <= bhi;
+  };
   auto bin_of = [&](uint64_t c) {
     const uint32_t d = (uint32_t)(c >> 32) - blo;
     return small ? d : min(__umulhi(d, mul), (uint32_t)kFastBins - 1u);
   };
-  // ---- 2. histogram ----
+  uint32_t b = 0, need = 0, in_bin = 0;
+  for (int pass = 0;; ++pass) {
+    const uint32_t range = bhi - blo;
+    small = range < (uint32_t)kFastBins;
+    mul = small ? 0u
+                : (uint32_t)((float)kFastBins * 4294967296.0f / ((float)range + 1.0f) * 0.99999f);
+    // ---- 2. histogram ----
 #pragma unroll
-  for (int i = 0; i < KP; ++i)
-    if (key[i] != 0ull) atomicAdd(&sh.hist[bin_of(key[i])], 1u);
-  __syncthreads();
-  // ---- 3. wave 0: the threshold bin.  Lane l holds bins 256*q + 4*l + e;
-  // bins descend with q, then lane, then e ----
-  if (wave == 0) {
-    uint32_t c[kFastQ][4], tq[kFastQ], incl[kFastQ], qtot[kFastQ];
-#pragma unroll
-    for (int q = 0; q < kFastQ; ++q) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(&sh.hist[(q * 64 + lane) * 4]);
-      c[q][0] = x.x;
-      c[q][1] = x.y;
-      c[q][2] = x.z;
-      c[q][3] = x.w;
-      tq[q] = x.x + x.y + x.z + x.w;
-    }
-#pragma unroll
-    for (int q = 0; q < kFastQ; ++q) {
-      incl[q] = wave_incl_scan_u32(tq[q]);
-      qtot[q] = (uint32_t)__builtin_amdgcn_readlane((int)incl[q], 63);
-    }
-    uint32_t total = 0;
-#pragma unroll
-    for (int q = 0; q < kFastQ; ++q) total += qtot[q];
-    // the (q, lane) holding the threshold bin, and the keys above that lane
-    uint32_t fq = 0, above_fq = 0, base = 0;
-    uint64_t own = 0ull;
-#pragma unroll
-    for (int q = kFastQ - 1; q >= 0; --q) {
-      const uint32_t above_l = base + qtot[q] - incl[q];  // bins of higher q or higher lanes
-      const uint64_t m = __ballot(above_l < k && above_l + tq[q] >= k);
-      if (own == 0ull && m != 0ull) {  // wave-uniform
-        own = m;
-        fq = (uint32_t)q;
-        above_fq = above_l;
-      }
-      base += qtot[q];
-    }
-    const int L = own != 0ull ? __ffsll((unsigned long long)own) - 1 : 0;
-    uint32_t cf[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      cf[e] = c[0][e];
-#pragma unroll
-      for (int q = 1; q < kFastQ; ++q)
-        if (fq == (uint32_t)q) cf[e] = c[q][e];
-    }
-    uint32_t bsel = 0, babove = 0, bcnt = 0, acc = above_fq;
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (acc < k && acc + cf[e] >= k) {
-        bsel = 256u * fq + 4u * (uint32_t)lane + (uint32_t)e;
-        babove = acc;
-        bcnt = cf[e];
-      }
-      acc += cf[e];
-    }
-    const uint32_t vb = (uint32_t)__builtin_amdgcn_readlane((int)bsel, L);
-    const uint32_t va = (uint32_t)__builtin_amdgcn_readlane((int)babove, L);
-    const uint32_t vc = (uint32_t)__builtin_amdgcn_readlane((int)bcnt, L);
-    if (lane == 0) {
-      sh.bin = vb;
-      sh.need = k - va;
-      sh.in_bin = vc;
-      sh.total = total;
-    }
-  }
-  __syncthreads();
-  const uint32_t b = sh.bin, need = sh.need, in_bin = sh.in_bin;
-  if (sh.total < k || in_bin > (uint32_t)kFastBinCap) {
+    for (int i = 0; i < KP; ++i)
+      if (in_play(key[i])) atomicAdd(&sh.hist[bin_of(key[i])], 1u);
     __syncthreads();
-    return false;
+    // ---- 3. wave 0: the threshold bin.  Lane l holds bins 256*q + 4*l + e;
+    // bins descend with q, then lane, then e ----
+    if (wave == 0) {
+      uint32_t c[kFastQ][4], tq[kFastQ], incl[kFastQ], qtot[kFastQ];
+#pragma unroll
+      for (int q = 0; q < kFastQ; ++q) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&sh.hist[(q * 64 + lane) * 4]);
+        c[q][0] = x.x;
+        c[q][1] = x.y;
+        c[q][2] = x.z;
+        c[q][3] = x.w;
+        tq[q] = x.x + x.y + x.z + x.w;
+      }
+#pragma unroll
+      for (int q = 0; q < kFastQ; ++q) {
+        incl[q] = wave_incl_scan_u32(tq[q]);
+        qtot[q] = (uint32_t)__builtin_amdgcn_readlane((int)incl[q], 63);
+      }
+      uint32_t total = 0;
+#pragma unroll
+      for (int q = 0; q < kFastQ; ++q) total += qtot[q];
+      // the (q, lane) holding the threshold bin, and the keys above that lane
+      uint32_t fq = 0, above_fq = 0, base = 0;
+      uint64_t own = 0ull;
+#pragma unroll
+      for (int q = kFastQ - 1; q >= 0; --q) {
+        const uint32_t above_l = base + qtot[q] - incl[q];  // bins of higher q or higher lanes
+        const uint64_t m = __ballot(above_l < kk && above_l + tq[q] >= kk);
+        if (own == 0ull && m != 0ull) {  // wave-uniform
+          own = m;
+          fq = (uint32_t)q;
+          above_fq = above_l;
+        }
+        base += qtot[q];
+      }
+      const int L = own != 0ull ? __ffsll((unsigned long long)own) - 1 : 0;
+      uint32_t cf[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cf[e] = c[0][e];
+#pragma unroll
+        for (int q = 1; q < kFastQ; ++q)
+          if (fq == (uint32_t)q) cf[e] = c[q][e];
+      }
+      uint32_t bsel = 0, babove = 0, bcnt = 0, acc = above_fq;
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        if (acc < kk && acc + cf[e] >= kk) {
+          bsel = 256u * fq + 4u * (uint32_t)lane + (uint32_t)e;
+          babove = acc;
+          bcnt = cf[e];
+        }
+        acc += cf[e];
+      }
+      const uint32_t vb = (uint32_t)__builtin_amdgcn_readlane((int)bsel, L);
+      const uint32_t va = (uint32_t)__builtin_amdgcn_readlane((int)babove, L);
+      const uint32_t vc = (uint32_t)__builtin_amdgcn_readlane((int)bcnt, L);
+      if (lane == 0) {
+        sh.bin = vb;
+        sh.need = kk - va;
+        sh.in_bin = vc;
+        sh.total = total;
+      }
+    }
+    __syncthreads();
+    b = sh.bin;
+    need = sh.need;
+    in_bin = sh.in_bin;
+    if (sh.total < kk) {
+      __syncthreads();
+      return false;
+    }
+    if (in_bin <= (uint32_t)kFastBinCap) break;
+    if (small || pass == 2) {  // one score value per bin already, or still crowded
+      __syncthreads();
+      return false;
+    }
+    // ---- narrow to the threshold bin: its keys' range, a cleared histogram ----
+    uint32_t nlo = 0xFFFFFFFFu, nhi = 0u;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      if (in_play(key[i]) && bin_of(key[i]) == b) {
+        const uint32_t h = (uint32_t)(key[i] >> 32);
+        nlo = min(nlo, h);
+        nhi = max(nhi, h);
+      }
+    }
+    nlo = wave_min_u32(nlo);
+    nhi = wave_max_u32(nhi);
+    // (wave 0 read the histogram before the last barrier, and every wave
+    // read wmin / wmax before the one ahead of the histogram)
+    for (int e = tid; e < kFastBins; e += NT) sh.hist[e] = 0u;
+    if (lane == 0) {
+      sh.wmin[wave] = nlo;
+      sh.wmax[wave] = nhi;
+    }
+    __syncthreads();
+    blo = wave_min_u32(lane < W ? sh.wmin[lane] : 0xFFFFFFFFu);
+    bhi = wave_max_u32(lane < W ? sh.wmax[lane] : 0u);
+    kk = need;
+    if (bhi == blo) {  // the bin is one score value: ties the bins cannot split
+      __syncthreads();
+      return false;
+    }
   }
   // ---- 4. the bin's keys, each wave's in its own region; wave 0 ranks ----
   uint32_t woff = 0;
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
-    const bool inb = key[i] != 0ull && bin_of(key[i]) == b;
+    const bool inb = in_play(key[i]) && bin_of(key[i]) == b;
     const uint64_t m = __ballot(inb);
     if (inb) sh.wb[wave][woff + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = key[i];
     woff += (uint32_t)__popcll(m);
