@@ -605,7 +605,8 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
       sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.seq_kv[t],
       sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
-      sl.blocks_per_group, u.f, u.s, selrow, (uint32_t)row_begin, (uint32_t)row_begin + win);
+      sl.blocks_per_group, sl.lists_complete != 0, u.f, u.s, selrow, (uint32_t)row_begin,
+      (uint32_t)row_begin + win);
 
   if (tid < kHeadsPerWg * QPR)
     *reinterpret_cast<u32x4*>(&qlds[hl * (D + 8) + (tid - hl * QPR) * 8]) = qv;
@@ -816,6 +817,16 @@ hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStre
 
 bool select_attend_fits(int T, int n_heads, int max_rows, int split_tiles) {
   return T > 0 && fused_fits(plan_splits(T, n_heads, max_rows, split_tiles), T, n_heads);
+}
+
+int step_split_tiles(int T, int n_heads, int max_rows) {
+  if (select_attend_fits(T, n_heads, max_rows, kStepSplitTiles)) return kStepSplitTiles;
+  const int n_tiles = max_rows > 0 ? (max_rows + kRT - 1) / kRT : 1;
+  const int n_hg = (n_heads + kHeadsPerWg - 1) / kHeadsPerWg;
+  int64_t want = (kStepTargetWgs + (int64_t)T * n_hg - 1) / ((int64_t)T * n_hg);
+  if (want < 1) want = 1;
+  if (want > n_tiles) want = n_tiles;
+  return (int)((n_tiles + want - 1) / want);
 }
 
 hipError_t launch_select_attend(const SelectLaunch& sl, const AttendLaunch& a, hipStream_t s) {

@@ -437,10 +437,17 @@ struct SelectLaunch {
   int ratio, top_k;
   const uint64_t* cand; const uint64_t* gcut;
   int list_len, groups_per_token, blocks_per_group;
+  int lists_complete;  // 1: the lists are the whole candidate set, for rows of any length
   int32_t* idx; int32_t* count;
   uint32_t* err;
 };
 bool select_attend_fits(int T, int n_heads, int max_rows, int split_tiles);
+// 64-row tiles per split of the decode step's attention: kStepSplitTiles when
+// the select runs inside the attention kernel (small batches); otherwise as
+// many as give about kStepTargetWgs workgroups (fewer, longer splits: less
+// partial-output traffic for the combine).
+constexpr int kStepTargetWgs = 512;
+int step_split_tiles(int T, int n_heads, int max_rows);
 hipError_t launch_select_attend(const SelectLaunch& s, const AttendLaunch& a, hipStream_t st);
 hipError_t launch_step_select(const SelectLaunch& s, int T, hipStream_t st);
 

@@ -450,7 +450,11 @@ IndexPlan plan_index(int T, int64_t ld) {
   const int64_t total = tiles * (T > 0 ? T : 1);
   int64_t tpw = (total + kWaves * 256 - 1) / (kWaves * 256);
   if (tpw < 1) tpw = 1;
-  if (tpw > kMaxTpw) tpw = kMaxTpw;
+  // A batch of rows of different lengths is planned for its longest; half
+  // the tiles per wave then keeps the workgroups of the longer rows from
+  // running alone at the end (large prefill chunks keep the full length).
+  const int cap = T > 1 && T <= 512 ? kMaxTpw / 2 : kMaxTpw;
+  if (tpw > cap) tpw = cap;
   p.tiles_per_wave = (int)tpw;
   p.wgs_per_token = (int)((tiles + kWaves * tpw - 1) / (kWaves * tpw));
   return p;

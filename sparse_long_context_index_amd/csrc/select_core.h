@@ -975,18 +975,20 @@ __device__ __forceinline__ bool fast_select(const uint64_t (&key)[KP], const uin
   return true;
 }
 
-// The decode step's select of one token: the fast select over four register
+// The decode step's select of one token: the fast select over KP register
 // keys per thread (the token's candidate lists, or every visible block of a
-// short row), and select_token when the fast select gives up or the keys do
-// not fit.  fsh and ssh may overlay each other.  Same contract as
+// row of at most KP*NT blocks), and select_token when the fast select gives
+// up or the keys do not fit.  lists_complete: the lists are the whole
+// candidate set (the E4M3 prefilter's rescored keys), to be used whatever
+// the row's length.  fsh and ssh may overlay each other.  Same contract as
 // select_token.
-template <int NT>
+template <int NT, int KP = 4>
 __device__ __forceinline__ SelResult step_select(
     const float* __restrict__ srow, int64_t ld, int64_t pos_t, int32_t ncomp_t, int ratio,
     int64_t key_row0, int64_t key_rows, int top_k, const uint64_t* __restrict__ cand,
     const uint64_t* __restrict__ gcut, int list_len, int groups_per_token, int blocks_per_group,
-    FastShared<NT>& fsh, SelShared<NT>& ssh, int32_t* dst, uint32_t e_lo, uint32_t e_hi) {
-  constexpr int KP = 4;
+    bool lists_complete, FastShared<NT>& fsh, SelShared<NT>& ssh, int32_t* dst, uint32_t e_lo,
+    uint32_t e_hi) {
   constexpr int GB = kMaxGroups / NT;
   const uint32_t tid = threadIdx.x;
   const uint32_t L = list_len > 0 ? (uint32_t)list_len : 1u;
@@ -1023,7 +1025,20 @@ __device__ __forceinline__ SelResult step_select(
     return res;
   }
   bool ok = false;
-  if (lists) {
+  if (lists && !lists_complete && n_vis <= (int64_t)(KP * NT)) {
+    // a row short enough to hold every block beats its lists (which may hold
+    // fewer than top_k keys): its scores, in one more round trip
+#pragma unroll
+    for (int i = 0; i < KP; ++i) sv[i] = srow[min(tid * KP + (uint32_t)i, (uint32_t)n_vis - 1u)];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const uint32_t j = tid * KP + (uint32_t)i;
+      key[i] = j < (uint32_t)n_vis ? block_key(sv[i], j) : 0ull;
+    }
+#pragma unroll
+    for (int g = 0; g < GB; ++g) gb[g] = 0ull;
+    ok = fast_select<NT, KP, GB>(key, gb, k_eff, fsh, dst, e_lo, e_hi, &res.emitted);
+  } else if (lists) {
     // the candidate lists of the groups that cover the row
     const uint32_t G = (uint32_t)blocks_per_group;
     const uint32_t ng = ((uint32_t)n_vis + G - 1u) / G;

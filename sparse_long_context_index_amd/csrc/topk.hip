@@ -37,7 +37,11 @@ __global__ __launch_bounds__(sel::kThreads) void topk_select_kernel(
 
 // The decode step's top-k for larger batches: one workgroup per token, the
 // fast select (select_token when it gives up), the selection written straight
-// to idx in ascending block order and padded with -1.
+// to idx in ascending block order and padded with -1.  KP key slots per
+// thread: with twelve, rows of up to 12,288 blocks select over all their
+// blocks (the shorter rows of a ragged batch, whose lists would hold too few
+// keys); four do a third of the per-slot work on a long row's lists.
+template <int KP>
 __global__ __launch_bounds__(sel::kThreads) void step_select_kernel(SelectLaunch sl) {
   __shared__ union {
     sel::SelShared<sel::kThreads> s;
@@ -45,11 +49,11 @@ __global__ __launch_bounds__(sel::kThreads) void step_select_kernel(SelectLaunch
   } u;
   const int t = blockIdx.x;
   int32_t* out = sl.idx + (int64_t)t * sl.top_k;
-  const sel::SelResult r = sel::step_select<sel::kThreads>(
+  const sel::SelResult r = sel::step_select<sel::kThreads, KP>(
       sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.seq_kv[t],
       sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
-      sl.blocks_per_group, u.f, u.s, out, 0u, (uint32_t)sl.top_k);
+      sl.blocks_per_group, sl.lists_complete != 0, u.f, u.s, out, 0u, (uint32_t)sl.top_k);
   for (uint32_t i = threadIdx.x; i < (uint32_t)sl.top_k; i += sel::kThreads) {
     if (i >= r.emitted) out[i] = -1;
     else if (!r.listed) out[i] = (int32_t)i;
@@ -180,7 +184,11 @@ hipError_t launch_score_cands(const float* scores, int64_t ld, const int64_t* po
 
 hipError_t launch_step_select(const SelectLaunch& sl, int T, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(step_select_kernel, dim3((unsigned)T), dim3(sel::kThreads), 0, s, sl);
+  // a batch may mix row lengths; a single row is the long row its lists serve
+  if (T > 1)
+    hipLaunchKernelGGL(step_select_kernel<12>, dim3((unsigned)T), dim3(sel::kThreads), 0, s, sl);
+  else
+    hipLaunchKernelGGL(step_select_kernel<4>, dim3((unsigned)T), dim3(sel::kThreads), 0, s, sl);
   return hipGetLastError();
 }
 
