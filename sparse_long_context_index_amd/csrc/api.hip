@@ -135,7 +135,9 @@ StepWs step_ws_layout(const csa_step_args* a) {
     w.n_kv = off;
     if (!a->n_kv) off += align256((size_t)a->T * 4);
     w.attend = off;
-    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, a->top_k + a->window, kStepSplitTiles);
+    const int rows = a->top_k + a->window;
+    off += attend_ws_bytes(a->T, a->n_heads, a->head_dim, rows,
+                           step_split_tiles(a->T, a->n_heads, rows));
     if (a->idx_e4m3) {
       const size_t C = (size_t)prefilter_count(a->top_k);
       w.pre_idx = off;
@@ -395,7 +397,7 @@ csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* str
   L.b_cap = a->window;
   L.copy_out = a->all_kv; L.copy_stride = a->top_k + a->window; L.n_kv_out = n_kv;
   L.max_rows = a->top_k + a->window;
-  L.split_tiles = kStepSplitTiles;
+  L.split_tiles = step_split_tiles(a->T, a->n_heads, L.max_rows);
   SelectLaunch S{};
   S.scores = scores; S.ld = a->max_vis; S.pos = a->pos; S.n_comp = a->n_comp;
   S.seq_kv = a->seq_kv; S.k_rows = a->k_rows;
@@ -422,7 +424,7 @@ csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* str
     e = launch_rescore(R, st);
     if (e != hipSuccess) return hip_status(e);
     S.cand = R.key; S.gcut = R.gcut; S.list_len = C;
-    S.groups_per_token = 1; S.blocks_per_group = (int)a->max_vis;
+    S.groups_per_token = 1; S.blocks_per_group = (int)a->max_vis; S.lists_complete = 1;
   }
   if (select_attend_fits(a->T, a->n_heads, L.max_rows, L.split_tiles))
     return hip_status(launch_select_attend(S, L, st));
