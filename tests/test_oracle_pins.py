@@ -125,21 +125,25 @@ def test_indexer_one_hot_weight_is_single_head_relu():
         np.testing.assert_allclose(indexer_scores(q, w, K)[0], want, rtol=1e-12, atol=1e-13)
 
 
-def test_indexer_matches_pages_corrected_einsum():
-    """Post-probe rewrite, F3 prints the corrected scorer as a torch program:
-    einsum 'tnd,cd->tnc', ReLU, weight, sum over heads, then topk.  Run it in
-    fp64 and compare scores and the top-k set."""
+def test_indexer_matches_per_head_torch_products():
+    """Post-probe rewrite, F3: every head scores every key with one shared key
+    row, the products pass through ReLU, are weighted by the head's w and
+    summed over heads, and the top-k is taken over the sums.  Restated here
+    head by head with torch fp64 matrix-vector products and torch.topk, and
+    compared with the oracle's scores and top-k set."""
     r = np.random.default_rng(5)
     T, n_ih, ihd, n = 3, 8, 32, 300
     q = r.standard_normal((T, n_ih, ihd)); K = r.standard_normal((n, ihd)); w = r.standard_normal((T, n_ih))
-    qt, Kt, wt = map(torch.from_numpy, (q, K, w))
-    s = torch.relu(torch.einsum("tnd,cd->tnc", qt, Kt))
-    total = (s * wt.unsqueeze(-1)).sum(1)
-    _, idx = total.topk(min(40, n), -1)
+    Kt = torch.from_numpy(K)
     for t in range(T):
+        total = torch.zeros(n, dtype=torch.float64)
+        for h in range(n_ih):
+            logits = torch.mv(Kt, torch.from_numpy(q[t, h]))   # [n]: key s . q_h
+            total += float(w[t, h]) * torch.clamp(logits, min=0.0)
+        _, idx = torch.topk(total, min(40, n))
         I, _ = indexer_scores(q[t], w[t], K)
-        np.testing.assert_allclose(I, total[t].numpy(), rtol=1e-12, atol=1e-12)
-        assert set(select_top_blocks(I, 40).tolist()) == set(idx[t].tolist())
+        np.testing.assert_allclose(I, total.numpy(), rtol=1e-12, atol=1e-12)
+        assert set(select_top_blocks(I, 40).tolist()) == set(idx.tolist())
 
 
 def test_indexer_per_head_key_algebra_differs():
