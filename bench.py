@@ -23,7 +23,8 @@ Also reported:
                   the dense HCA step at 1M, the 32K step, a batch of 32
                   sequences of 16K..128K tokens, a 4096-token prefill chunk
                   (indexer as a fraction of bf16 MFMA peak) and the 1M step
-                  with E4M3 indexer keys;
+                  with E4M3 indexer keys and the producer side (compressors and
+                  cache append) for 1 and 32 tokens;
   cpu_baseline -- the fp64 numpy oracle timed on a bounded sample of the
                   headline workload on this host's cores (a reported baseline
                   only).
@@ -352,6 +353,7 @@ def main() -> int:
 
 def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dict:
     """The other workloads, each as graph replays of rotated layers."""
+    import numpy as np
     res = {}
 
     def csa_config(name, inp, n_layers, replays, e4m3=False, index_stage=False):
@@ -420,6 +422,49 @@ def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dic
     r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
     r["workload"] = "prefill chunk: 4096 query tokens at positions 61440..65535, 16384 blocks"
     res["prefill_4096"] = r
+
+    # producer side: the compressors and cache append of one decode step
+    for T in (1, 32):
+        log(f"config: producer step, {T} token(s)")
+        pinp = gen.producer_1m(T=T)
+        nl = LAYERS
+        bfp = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+        i64 = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)  # noqa: E731
+        x = bfp(pinp.x)
+        wk0, wi0 = bfp(pinp.w_kv), bfp(pinp.w_ik)
+        wks = [wk0] + [wk0.clone() for _ in range(nl - 1)]
+        wis = [wi0] + [wi0.clone() for _ in range(nl - 1)]
+        st = dict(seq=i64(pinp.seq, np.int32), pos=i64(pinp.pos, np.int64),
+                  ring=i64(pinp.ring, np.float32), swa=bfp(pinp.swa),
+                  swa_head=i64(pinp.swa_head, np.int32), swa_len=i64(pinp.swa_len, np.int32),
+                  comp_kv=bfp(pinp.comp_kv), k_idx=bfp(pinp.k_idx),
+                  seq_kv=i64(pinp.seq_kv, np.int64), n_comp=i64(pinp.n_comp, np.int32))
+        pws = torch.empty(B.csa_compress_append_workspace_bytes(T, pinp.H, pinp.hd, pinp.ihd),
+                          dtype=torch.uint8, device=dev)
+        perr = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def pcall(i):
+            return lambda: B.csa_compress_append(
+                x, wks[i], wis[i], st["seq"], st["pos"], pinp.ratio, pinp.window, st["ring"],
+                st["swa"], st["swa_head"], st["swa_len"], st["comp_kv"], st["k_idx"],
+                st["seq_kv"], st["n_comp"], pws, err=perr)
+        g = R.capture([pcall(i) for i in range(nl)])
+        ms = R.replays(g, nl, 20)
+        torch.cuda.synchronize()
+        # the same positions are replayed: the appends repeat the same rows
+        # and may flag the n_comp bookkeeping; only range errors count here
+        if int(perr.item()) & ~0x4:
+            raise RuntimeError(f"producer: device error word {int(perr.item()):#x}")
+        wbytes = (2 * pinp.hd + 2 * pinp.ihd) * pinp.H * 2
+        pb = wbytes + T * (pinp.H * 2 + (2 * pinp.hd + 2 * pinp.ihd) * 4 + pinp.hd * 2)
+        r = {"step_us": _dist_us(ms), "min_bytes": pb}
+        r["gbs"] = round(pb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
+        r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+        r["workload"] = (f"producer of one decode step, {T} token(s): both compressors' "
+                         "projections (H 7168 -> 2x512 + 2x128), ring, window append, pooling")
+        res[f"producer_{T}"] = r
+        del wks, wis, g, st, pws
+        torch.cuda.empty_cache()
 
     # dense HCA at 1M
     log("config: dense HCA step at 1M")

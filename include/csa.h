@@ -256,6 +256,49 @@ size_t csa_decode_step_workspace_bytes(const csa_step_args* a);
 csa_status csa_decode_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Producer side of one decode step: the compressors and the cache append
+ * (1M-context audit, D1/D2: a main and an indexer-key compressor of the form
+ * Compressor(ratio, width, H), projecting the hidden state to 2 x width per
+ * token, compressed rows width wide; its closing assessment: overlapped
+ * 2m-token windows with softmax weights; D5: the sliding-window ring).  For
+ * each token t, of sequence s = seq[t] (the tokens of one call belong to
+ * distinct sequences) at position p = pos[t]:
+ *   y = [w_kv; w_ik] . x[t]                       (fp32: c_kv | z_kv | c_ik | z_ik)
+ *   ring[s, p mod 2*ratio] = y
+ *   swa[s, swa_head[s]] = bf16(c_kv); swa_head[s] = (swa_head[s] + 1) mod window;
+ *   swa_len[s] = min(swa_len[s] + 1, window)
+ *   if (p + 1) mod ratio == 0, block i = (p + 1)/ratio - 1 is complete:
+ *     per channel, softmax over tokens j in [max(0, (i-1)*ratio), (i+1)*ratio)
+ *     of z_j weighting c_j (read from the ring), in bf16 to
+ *     comp_kv[seq_kv[s] + i] (width hd) and k_idx[seq_kv[s] + i] (width ihd);
+ *     n_comp[s] = i + 1.
+ * Reading of the pages: the projection's two halves are values and scores;
+ * the window row of a token is its main value half.
+ *   x [T, H] bf16; w_kv [2*hd, H], w_ik [2*ihd, H] bf16, one output channel per
+ *   row; ring [S, 2*ratio, 2*hd + 2*ihd] fp32 (the last 2*ratio tokens'
+ *   projections, kept between calls); swa [S, window, hd] bf16;
+ *   swa_head, swa_len, n_comp [S] int32; seq [T] int32; pos [T] int64;
+ *   seq_kv [S] int64, the row of each sequence's block 0 (only the row
+ *   written, seq_kv[s] + i, must lie in [0, comp_rows)); comp_kv
+ *   [comp_rows, hd] and k_idx [comp_rows, ihd] bf16.
+ *   ws >= csa_compress_append_workspace_bytes(T, H, hd, ihd), 256-B aligned.
+ * Device errors (in *err): CSA_DERR_BAD_META for a sequence id, position or
+ * ring head out of range, or n_comp[s] != i at a block end (the row is still
+ * written); CSA_DERR_KEY_RANGE for a compressed row outside comp_rows (not
+ * written).
+ * Supported: H a multiple of 256; hd, ihd multiples of 16 (hd <= 1024,
+ * ihd <= 512); ratio a power of two up to 16; window <= 1024.
+ */
+size_t csa_compress_append_workspace_bytes(int T, int H, int hd, int ihd);
+csa_status csa_compress_append(const uint16_t* x, int T, int H, const uint16_t* w_kv, int hd,
+                               const uint16_t* w_ik, int ihd, const int32_t* seq,
+                               const int64_t* pos, int S, int ratio, int window, float* ring,
+                               uint16_t* swa, int32_t* swa_head, int32_t* swa_len,
+                               uint16_t* comp_kv, uint16_t* k_idx, const int64_t* seq_kv,
+                               int32_t* n_comp, int64_t comp_rows, void* ws, size_t ws_bytes,
+                               uint32_t* err, void* stream);
+
+/*
  * One stage of csa_decode_step, for callers that schedule other work between
  * the indexer and the rest of the step, or time the stages apart.
  *   stage CSA_STAGE_INDEX: S1 -- the indexer scores and the candidate lists

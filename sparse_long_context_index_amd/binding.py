@@ -70,6 +70,10 @@ _SIGS = {
     "csa_decode_step_workspace_bytes": (_sz, [ctypes.POINTER(StepArgs)]),
     "csa_decode_step": (_i32, [ctypes.POINTER(StepArgs), _vp, _sz, _vp]),
     "csa_decode_step_noalloc": (_i32, [ctypes.POINTER(StepArgs), _vp]),
+    "csa_compress_append_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "csa_compress_append": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
+                                   _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _sz,
+                                   _vp, _vp]),
     "csa_decode_step_stage": (_i32, [ctypes.POINTER(StepArgs), _i32, _vp, _sz, _vp]),
 }
 EXPORTS = tuple(_SIGS)
@@ -226,6 +230,29 @@ def csa_decode_step_stage(args: StepArgs, stage: int, ws, stream=None):
     _check("csa_decode_step_stage", load().csa_decode_step_stage(
         ctypes.byref(args), int(stage), _p(ws, (torch.uint8,), "ws", True),
         0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def csa_compress_append_workspace_bytes(T, H, hd, ihd) -> int:
+    return int(load().csa_compress_append_workspace_bytes(T, H, hd, ihd))
+
+
+def csa_compress_append(x, w_kv, w_ik, seq, pos, ratio, window, ring, swa, swa_head, swa_len,
+                        comp_kv, k_idx, seq_kv, n_comp, ws, err=None, stream=None):
+    """x [T, H] bf16; w_kv [2hd, H], w_ik [2ihd, H] bf16; ring [S, 2*ratio,
+    2hd + 2ihd] fp32; swa [S, window, hd] bf16; comp_kv [rows, hd], k_idx
+    [rows, ihd] bf16; per sequence swa_head, swa_len, n_comp int32, seq_kv
+    int64; per token seq int32, pos int64."""
+    T, H = int(x.shape[0]), int(x.shape[1])
+    hd, ihd, S = int(w_kv.shape[0]) // 2, int(w_ik.shape[0]) // 2, int(ring.shape[0])
+    _check("csa_compress_append", load().csa_compress_append(
+        _p(x, _BF16, "x"), T, H, _p(w_kv, _BF16, "w_kv"), hd, _p(w_ik, _BF16, "w_ik"), ihd,
+        _p(seq, (torch.int32,), "seq"), _p(pos, (torch.int64,), "pos"), S, ratio, window,
+        _p(ring, (torch.float32,), "ring"), _p(swa, _BF16, "swa"),
+        _p(swa_head, (torch.int32,), "swa_head"), _p(swa_len, (torch.int32,), "swa_len"),
+        _p(comp_kv, _BF16, "comp_kv"), _p(k_idx, _BF16, "k_idx"),
+        _p(seq_kv, (torch.int64,), "seq_kv"), _p(n_comp, (torch.int32,), "n_comp"),
+        int(comp_kv.shape[0]), _p(ws, (torch.uint8,), "ws", True), 0 if ws is None else ws.numel(),
+        _p(err, (torch.int32, torch.uint32), "err", optional=True), _stream(stream)))
 
 
 def csa_decode_step_noalloc(args: StepArgs, stream=None):

@@ -458,4 +458,39 @@ csa_status csa_decode_step_noalloc(const csa_step_args* a, void* stream) {
   return csa_decode_step(a, ws, (size_t)CSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+size_t csa_compress_append_workspace_bytes(int T, int H, int hd, int ihd) {
+  if (T <= 0 || H <= 0 || hd <= 0 || ihd <= 0) return 0;
+  return compress_ws_bytes(T, H, hd, ihd);
+}
+
+csa_status csa_compress_append(const uint16_t* x, int T, int H, const uint16_t* w_kv, int hd,
+                               const uint16_t* w_ik, int ihd, const int32_t* seq,
+                               const int64_t* pos, int S, int ratio, int window, float* ring,
+                               uint16_t* swa, int32_t* swa_head, int32_t* swa_len,
+                               uint16_t* comp_kv, uint16_t* k_idx, const int64_t* seq_kv,
+                               int32_t* n_comp, int64_t comp_rows, void* ws, size_t ws_bytes,
+                               uint32_t* err, void* stream) {
+  if (T < 0 || H < 1 || hd < 1 || ihd < 1 || S < 1 || ratio < 1 || window < 1 || comp_rows < 0)
+    return CSA_EINVAL;
+  if (!x || !w_kv || !w_ik || !seq || !pos || !ring || !swa || !swa_head || !swa_len ||
+      !comp_kv || !k_idx || !seq_kv || !n_comp)
+    return CSA_EINVAL;
+  if (!aligned16(x) || !aligned16(w_kv) || !aligned16(w_ik) || !aligned4(ring) ||
+      !aligned4(seq) || !aligned4(swa_head) || !aligned4(swa_len) || !aligned4(n_comp))
+    return CSA_EINVAL;
+  if (H % 256 != 0 || hd % 16 != 0 || ihd % 16 != 0 || hd > 1024 || ihd > 512 ||
+      (ratio & (ratio - 1)) != 0 || ratio > 16 || window > 1024 || T > kMaxGridY * 32)
+    return CSA_EUNSUPPORTED;
+  if (T == 0) return CSA_OK;
+  csa_status st = check_ws(ws, ws_bytes, compress_ws_bytes(T, H, hd, ihd));
+  if (st != CSA_OK) return st;
+  CompressLaunch c{};
+  c.x = x; c.T = T; c.H = H; c.w_kv = w_kv; c.hd = hd; c.w_ik = w_ik; c.ihd = ihd;
+  c.seq = seq; c.pos = pos; c.S = S; c.ratio = ratio; c.window = window;
+  c.ring = ring; c.swa = swa; c.swa_head = swa_head; c.swa_len = swa_len;
+  c.comp_kv = comp_kv; c.k_idx = k_idx; c.seq_kv = seq_kv; c.n_comp = n_comp;
+  c.comp_rows = comp_rows; c.ws = ws; c.err = err;
+  return hip_status(launch_compress_append(c, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

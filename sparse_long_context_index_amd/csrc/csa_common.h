@@ -356,6 +356,20 @@ struct RescoreLaunch {
   uint64_t* key; uint64_t* gcut;
 };
 hipError_t launch_rescore(const RescoreLaunch& a, hipStream_t s);
+// The producer side of one decode step (produce.hip): both compressors'
+// projections of the new tokens, the ring of recent projections, the
+// sliding-window append and, at block ends, the pooled compressed rows.
+struct CompressLaunch {
+  const uint16_t* x; int T, H;
+  const uint16_t* w_kv; int hd; const uint16_t* w_ik; int ihd;
+  const int32_t* seq; const int64_t* pos; int S, ratio, window;
+  float* ring; uint16_t* swa; int32_t* swa_head; int32_t* swa_len;
+  uint16_t* comp_kv; uint16_t* k_idx; const int64_t* seq_kv; int32_t* n_comp; int64_t comp_rows;
+  void* ws; uint32_t* err;
+};
+size_t compress_ws_bytes(int T, int H, int hd, int ihd);
+hipError_t launch_compress_append(const CompressLaunch& c, hipStream_t s);
+
 // Row quantisation to E4M3 with one power-of-two scale per row (quant.hip).
 hipError_t launch_quant_e4m3(const uint16_t* src, int64_t rows, int d, uint8_t* codes,
                              float* scale, hipStream_t s);

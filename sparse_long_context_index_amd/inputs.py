@@ -280,3 +280,80 @@ def prefill(seed: int = 4, T: int = 4096, ctx: int = 65536) -> CSAInputs:
 
 WORKLOADS = {"tiny": tiny, "32k": ctx32k, "1m": ctx1m, "batched": batched,
              "prefill": prefill}
+
+
+# ---------------------------------------------------------------------------
+# Producer side (compressors and cache append) of one decode step.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ProducerInputs:
+    """One decode step's producer inputs and the per-sequence state before it.
+
+    x [T, H] bf16 bits; w_kv [2*hd, H], w_ik [2*ihd, H] bf16 bits (one output
+    channel per row, N(0, 1/H)); seq [T] int32 (distinct); pos [T] int64;
+    ring [S, 2*ratio, 2*hd + 2*ihd] float32; swa [S, window, hd] bf16 bits;
+    swa_head, swa_len, n_comp [S] int32; seq_kv [S] int64; comp_kv
+    [rows, hd] and k_idx [rows, ihd] bf16 bits."""
+
+    H: int
+    hd: int
+    ihd: int
+    ratio: int
+    window: int
+    x: np.ndarray
+    w_kv: np.ndarray
+    w_ik: np.ndarray
+    seq: np.ndarray
+    pos: np.ndarray
+    ring: np.ndarray
+    swa: np.ndarray
+    swa_head: np.ndarray
+    swa_len: np.ndarray
+    n_comp: np.ndarray
+    seq_kv: np.ndarray
+    comp_kv: np.ndarray
+    k_idx: np.ndarray
+
+    @property
+    def T(self) -> int:
+        return int(self.pos.shape[0])
+
+
+def producer(seed: int, *, S: int, T: int, H: int, hd: int, ihd: int, ratio: int, window: int,
+             max_pos: int) -> ProducerInputs:
+    """Draw T tokens of T distinct sequences (of S) at positions in
+    [0, max_pos), with a consistent state: n_comp = floor(pos/ratio) stored
+    blocks, a window ring holding min(pos, window) rows with its head at
+    pos mod window, and a ring of earlier projections drawn as N(0, 1).
+    Draw order: x, w_kv, w_ik, ring, swa, comp_kv, k_idx, then the choices."""
+    rng = np.random.default_rng(seed)
+    f = np.float32
+    x = f32_to_bf16_bits(rng.standard_normal((T, H), dtype=f))
+    w_kv = f32_to_bf16_bits((rng.standard_normal((2 * hd, H), dtype=f) / np.sqrt(H)).astype(f))
+    w_ik = f32_to_bf16_bits((rng.standard_normal((2 * ihd, H), dtype=f) / np.sqrt(H)).astype(f))
+    ring = rng.standard_normal((S, 2 * ratio, 2 * hd + 2 * ihd), dtype=f)
+    swa = f32_to_bf16_bits(rng.standard_normal((S, window, hd), dtype=f))
+    seq = np.sort(rng.choice(S, size=T, replace=False)).astype(np.int32)
+    pos_s = rng.integers(0, max_pos, size=S).astype(np.int64)
+    n_comp = (pos_s // ratio).astype(np.int32)
+    # The compressed caches are represented by their last two rows per
+    # sequence (the producer writes only row seq_kv + n_comp): sequence s's
+    # block n_comp lands on row 2s + 1, so seq_kv[s] = 2s + 1 - n_comp (the
+    # rows of its earlier blocks are not materialised).
+    seq_kv = (2 * np.arange(S, dtype=np.int64) + 1 - n_comp.astype(np.int64))
+    rows = 2 * S
+    comp_kv = f32_to_bf16_bits(rng.standard_normal((rows, hd), dtype=f))
+    k_idx = f32_to_bf16_bits(rng.standard_normal((rows, ihd), dtype=f))
+    return ProducerInputs(
+        H=H, hd=hd, ihd=ihd, ratio=ratio, window=window, x=x, w_kv=w_kv, w_ik=w_ik, seq=seq,
+        pos=pos_s[seq], ring=ring, swa=swa, swa_head=(pos_s % window).astype(np.int32),
+        swa_len=np.minimum(pos_s, window).astype(np.int32), n_comp=n_comp, seq_kv=seq_kv,
+        comp_kv=comp_kv, k_idx=k_idx)
+
+
+def producer_1m(seed: int = 5, T: int = 1) -> ProducerInputs:
+    """The producer of the 1M-context layer: H 7168, hd 512, ihd 128, ratio 4,
+    window 128; T sequences (of 64) near 2^20 tokens."""
+    return producer(seed, S=64, T=T, H=7168, hd=512, ihd=128, ratio=4, window=128,
+                    max_pos=1 << 20)

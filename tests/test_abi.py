@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(b.EXPORTS)
@@ -197,3 +197,24 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4, dtype=torch.float32)
     with pytest.raises(ValueError, match="GPU tensor"):
         b._p(t, (torch.float32,), "x")
+
+
+def test_compress_append_validation(lib):
+    f = lambda **kw: lib.csa_compress_append(*{**dict(  # noqa: E731
+        x=FAKE, T=1, H=7168, w_kv=FAKE, hd=512, w_ik=FAKE, ihd=128, seq=FAKE, pos=FAKE, S=4,
+        ratio=4, window=128, ring=FAKE, swa=FAKE, swa_head=FAKE, swa_len=FAKE, comp_kv=FAKE,
+        k_idx=FAKE, seq_kv=FAKE, n_comp=FAKE, comp_rows=8, ws=FAKE, ws_bytes=1 << 24,
+        err=None, stream=None), **kw}.values())
+    need = b.csa_compress_append_workspace_bytes(1, 7168, 512, 128)
+    # split-K partials: 7 chunks of 1024 x (2*512 + 2*128) fp32 for one token
+    assert need == 7 * 1280 * 4
+    assert f(T=0) == b.CSA_OK
+    assert f(x=None) == b.CSA_EINVAL
+    assert f(x=FAKE + 8) == b.CSA_EINVAL          # 16-byte loads of x rows
+    assert f(H=7000) == b.CSA_EUNSUPPORTED        # not a multiple of 256
+    assert f(hd=520) == b.CSA_EUNSUPPORTED
+    assert f(ratio=32) == b.CSA_EUNSUPPORTED and f(ratio=3) == b.CSA_EUNSUPPORTED
+    assert f(S=0) == b.CSA_EINVAL
+    assert f(ws_bytes=need - 1) == b.CSA_EWORKSPACE
+    assert f(ws=FAKE + 16) == b.CSA_EWORKSPACE
+
