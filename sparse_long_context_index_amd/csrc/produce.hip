@@ -59,6 +59,10 @@ __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict
       a[s] = *reinterpret_cast<const u32x4*>(wrow + k);
       b[s] = *reinterpret_cast<const u32x4*>(xrow + k);
     }
+    // keep every load ahead of the products: all 32 in flight at once (the
+    // scheduler would otherwise interleave them with the MFMAs, a few at a
+    // time, one round trip after another)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
