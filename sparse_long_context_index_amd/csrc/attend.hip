@@ -657,35 +657,48 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int
   const size_t sstride = (size_t)p.n_heads * D;
   const uint16_t* pbase = part_o + slot0 * D + lane * EPL;
 
-  float m_s = -INFINITY, l_s = 0.f;
-  if (tid < n_splits) {
-    const size_t slot = slot0 + (size_t)tid * p.n_heads;
-    m_s = part_ml[slot * 2];
-    l_s = part_ml[slot * 2 + 1];
+  // Every load is unconditional (split index clamped, value masked after):
+  // a load inside `if (s < n_splits)` waits for its data before the branch
+  // closes, which chained the round's loads one round trip after another.
+  float m_s, l_s;
+  {
+    const size_t slot = slot0 + (size_t)min(tid, n_splits - 1) * p.n_heads;
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + slot * 2);
+    m_s = tid < n_splits ? ml.x : -INFINITY;
+    l_s = tid < n_splits ? ml.y : 0.f;
   }
   float v[CH][EPL];
   auto load_round = [&](int c0) {
+    constexpr int NQ = EPL % 8 == 0 ? EPL / 8 : 1;
+    u32x4 raw[CH][NQ];
+    uint16_t raw1[CH][EPL % 8 == 0 ? 1 : EPL];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int s = wave + SG * (c0 + c);
+      const int s = min(wave + SG * (c0 + c), n_splits - 1);
+      const uint16_t* src = pbase + (size_t)s * sstride;
+      if constexpr (EPL % 8 == 0) {
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) v[c][j] = 0.f;
-      if (s < n_splits) {
-        const uint16_t* src = pbase + (size_t)s * sstride;
-        if constexpr (EPL % 8 == 0) {
+        for (int q = 0; q < NQ; ++q) raw[c][q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
+      } else {
 #pragma unroll
-          for (int j = 0; j < EPL; j += 8) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(src + j);
+        for (int j = 0; j < EPL; ++j) raw1[c][j] = src[j];
+      }
+    }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[c][j + 2 * e] = __uint_as_float(x[e] << 16);
-              v[c][j + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
-            }
+    for (int c = 0; c < CH; ++c) {
+      const bool ok = wave + SG * (c0 + c) < n_splits;
+      if constexpr (EPL % 8 == 0) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[c][8 * q + 2 * e] = ok ? __uint_as_float(raw[c][q][e] << 16) : 0.f;
+            v[c][8 * q + 2 * e + 1] = ok ? __uint_as_float(raw[c][q][e] & 0xFFFF0000u) : 0.f;
           }
-        } else {
-#pragma unroll
-          for (int j = 0; j < EPL; ++j) v[c][j] = bf16_to_f32(src[j]);
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) v[c][j] = ok ? bf16_to_f32(raw1[c][j]) : 0.f;
       }
     }
   };
