@@ -148,17 +148,18 @@ def test_compress_append_1m_shape(dev, T):
     assert n >= 1 and (T == 1 or len(out["pooled"]) < T)
 
 
-def test_compress_append_sequence_of_steps(dev):
-    say("csa_compress_append: 3 sequences, 21 decode steps each, small shapes")
-    S, H, hd, ihd, ratio, window = 3, 256, 16, 32, 4, 8
+@pytest.mark.parametrize("ratio", [1, 2, 4, 16])
+def test_compress_append_sequence_of_steps(dev, ratio):
+    say(f"csa_compress_append: 3 sequences, 21 decode steps each, ratio {ratio}, small shapes")
+    S, H, hd, ihd, window = 3, 256, 16, 32, 8
     p = gen.producer(11, S=S, T=S, H=H, hd=hd, ihd=ihd, ratio=ratio, window=window, max_pos=1)
     # fresh sequences at positions 0, 1, 2; empty rings; room for 8 blocks each
     p.ring[:] = 0.0
     p.swa[:] = 0
     p.swa_head[:] = [0, 1, 2]
     p.swa_len[:] = [0, 1, 2]
-    p.n_comp[:] = 0
-    rows = 8
+    p.n_comp[:] = np.array([0, 1, 2]) // ratio   # the blocks the earlier tokens completed
+    rows = 32
     p.seq_kv[:] = np.arange(S) * rows
     p.comp_kv = np.zeros((S * rows, hd), np.uint16)
     p.k_idx = np.zeros((S * rows, ihd), np.uint16)
@@ -182,7 +183,7 @@ def test_compress_append_sequence_of_steps(dev):
         p.swa_len = d["swa_len"].cpu().numpy()
         p.n_comp = d["n_comp"].cpu().numpy()
         p.comp_kv, p.k_idx = _bits(d["comp_kv"]), _bits(d["k_idx"])
-    assert p.n_comp.tolist() == [5, 5, 5]   # 21, 22, 23 tokens seen
+    assert p.n_comp.tolist() == [(int(s0) + 21) // ratio for s0 in start]  # 21, 22, 23 tokens seen
     assert p.swa_len.tolist() == [8, 8, 8]
 
 
