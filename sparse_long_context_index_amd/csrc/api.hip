@@ -113,6 +113,16 @@ struct StepWs {
   size_t scores, topk, idx, count, n_kv, attend, pre_idx, pre_count, pre_key, pre_gcut, total;
 };
 
+// Keys the step's select holds: four register slots per thread when it runs
+// inside the attention kernel (or for a single row), twelve in the select
+// kernel of a larger batch -- three times the candidates per group, so that
+// the lists of the shorter rows of a ragged batch rarely overflow.
+int step_pool(const csa_step_args* a) {
+  if (a->T <= 1 || select_attend_fits(a->T, a->n_heads, a->top_k + a->window, kStepSplitTiles))
+    return kStepPool;
+  return 3 * kStepPool;
+}
+
 // Candidates the E4M3 prefilter keeps: half as many again as top_k, at most
 // what the select holds in registers.
 int prefilter_count(int top_k) {
@@ -127,7 +137,7 @@ StepWs step_ws_layout(const csa_step_args* a) {
     w.scores = off;
     if (!a->scores) off += align256((size_t)a->T * (size_t)a->max_vis * 4);
     w.topk = off;
-    off += topk_ws_layout(nullptr, a->T, plan_topk(a->T, a->max_vis, a->top_k, kStepPool)).bytes;
+    off += topk_ws_layout(nullptr, a->T, plan_topk(a->T, a->max_vis, a->top_k, step_pool(a))).bytes;
     w.idx = off;
     if (!a->idx) off += align256((size_t)a->T * a->top_k * 4);
     w.count = off;
@@ -365,7 +375,7 @@ csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* str
   int32_t* idx = a->idx ? a->idx : reinterpret_cast<int32_t*>(base + lay.idx);
   int32_t* count = a->count ? a->count : reinterpret_cast<int32_t*>(base + lay.count);
   int32_t* n_kv = a->n_kv ? a->n_kv : reinterpret_cast<int32_t*>(base + lay.n_kv);
-  const TopkPlan tp = plan_topk(a->T, a->max_vis, a->top_k, kStepPool);
+  const TopkPlan tp = plan_topk(a->T, a->max_vis, a->top_k, step_pool(a));
   const TopkWs tw = topk_ws_layout(base + lay.topk, a->T, tp);
 
   // S1 with its candidate lists

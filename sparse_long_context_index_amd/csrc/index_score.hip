@@ -45,6 +45,9 @@ namespace {
 constexpr int kTileN = 32;
 constexpr int kWaves = kIndexWaves;
 constexpr int kMaxTpw = 8;  // tiles per wave (scores held in VGPRs)
+// Lists of up to this many keys are rebuilt by rounds of wave maxima; longer
+// ones by a rank merge (whose cost does not grow with the list).
+constexpr int kMergeRoundsMax = 8;
 
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
@@ -301,6 +304,28 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
             if (lane == 16) prev = r15;
             if (lane < m) rl = rl > k ? rl : (prev > k ? k : prev);
           }
+        } else if (nc > 0 && m > kMergeRoundsMax) {
+          // Rank merge of the list (lanes 0..31, sorted, descending) with the
+          // tile (lanes 32..63): a key's rank is the number of larger keys
+          // among the 64 (keys are unique where nonzero).  A list key's rank
+          // is its lane plus the tile keys above it; a tile key's, the list
+          // keys and the tile keys above it.  Each key then moves to the
+          // lane of its rank (ds_permute), which keeps the list sorted.
+          const uint64_t mine = half == 1 ? tkey : rl;
+          uint32_t rank = half == 1 ? 0u : (uint32_t)lane;
+#pragma unroll 8
+          for (int j = 0; j < 32; ++j) {
+            const uint64_t tj = readlane_u64(tkey, 32 + j);
+            const uint64_t lj = readlane_u64(rl, j);
+            rank += tj > mine ? 1u : 0u;
+            if (half == 1) rank += lj > mine ? 1u : 0u;
+          }
+          const uint32_t nnz = (uint32_t)__popcll(__ballot(mine != 0ull));
+          const int addr = (int)(min(rank, 63u) * 4u);
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)(mine >> 32));
+          const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)mine);
+          const uint64_t got = ((uint64_t)hi << 32) | lo;
+          if (lane < m) rl = (uint32_t)lane < nnz ? got : 0ull;
         } else if (nc > 0) {
           // wave_m rounds over the list (lanes 0..31) and the tile (lanes
           // 32..63): lane order is block order for equal scores
