@@ -460,7 +460,7 @@ bool select_attend_fits(int T, int n_heads, int max_rows, int split_tiles);
 // the select runs inside the attention kernel (small batches); otherwise as
 // many as give about kStepTargetWgs workgroups (fewer, longer splits: less
 // partial-output traffic for the combine).
-constexpr int kStepTargetWgs = 512;
+constexpr int kStepTargetWgs = 256;
 int step_split_tiles(int T, int n_heads, int max_rows);
 hipError_t launch_select_attend(const SelectLaunch& s, const AttendLaunch& a, hipStream_t st);
 hipError_t launch_step_select(const SelectLaunch& s, int T, hipStream_t st);
