@@ -130,8 +130,9 @@ def test_step_small_batch_list_paths(dev):
 
 def test_step_long_and_medium_rows(dev):
     """A 1M-context token next to one with 15,000 visible blocks: the shorter
-    row's lists (12 keys per 256-block group) hold fewer keys than top_k, so
-    its select runs over its whole row while the long row uses its lists."""
+    row's lists (16 keys per 1024-block group, the plan of the long row) hold
+    fewer keys than top_k, so its select runs over its whole row while the
+    long row uses its lists."""
     say("step T=2: 262,144 and 15,000 visible blocks")
     inp = gen.synth(26, pos=[ONE_M, 4 * 15000 + 1], seq_of_token=[0, 1],
                     n_comp_seq=[ONE_M // 4, 15000], **gen.MAIN)
