@@ -357,6 +357,225 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     cand_publish(rl, n_ok, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
 }
 
+// Batches of 2..kBatchMaxT rows: a persistent grid of one workgroup per CU
+// over the non-empty 256-block items (token, chunk) of all rows, each
+// workgroup taking a contiguous, equal share of them.  A grid of
+// (row, chunk) workgroups planned for the longest row leaves the shorter
+// rows' workgroups idle and ends in a partly filled round; here every CU
+// streams about the same number of tiles.  Wave w takes tile 8*chunk + w of
+// each item, with two tiles in flight across item boundaries; the query
+// block and head weights are reloaded (pipeline drained) when the token
+// changes.  Scores, candidate lists and their layout are those of
+// index_score_kernel with one tile per wave.
+constexpr int kBatchMaxT = 512;
+constexpr int kBatchGrid = 256;
+
+template <int IHD, int MT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_batch_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, int64_t k_rows, const int64_t* __restrict__ pos,
+    const int64_t* __restrict__ seq_kv, const int32_t* __restrict__ n_comp, int T, int n_ih,
+    int ratio, float* __restrict__ scores, int64_t ld, CandArgs ca, uint32_t* __restrict__ err) {
+  constexpr int KS = IHD / 16;
+  constexpr int RB = 2 * IHD;
+  constexpr int CPR = RB / 16;
+  constexpr int TILE_CHUNKS = kTileN * CPR;
+  constexpr int LPT = TILE_CHUNKS / 64;
+  constexpr int QCHUNKS = MT * 32 * CPR;
+  static_assert(kWaves * 2 * TILE_CHUNKS * 16 + QCHUNKS * 16 + (kBatchMaxT + 1) * 4 +
+                    kBatchMaxT * 12 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) u32x4 ktile[kWaves][2][TILE_CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4 qlds[QCHUNKS];
+  __shared__ uint32_t s_pref[kBatchMaxT + 1];  // items before token t
+  __shared__ int64_t s_row0[kBatchMaxT];
+  __shared__ int32_t s_nvis[kBatchMaxT];
+  __shared__ uint32_t s_wsum[kWaves];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+
+  // ---- every row's visible blocks and item count; a block-wide scan ----
+  uint32_t items = 0;
+  if (threadIdx.x < T) {
+    const int t = threadIdx.x;
+    uint32_t flags = 0;
+    int64_t n_vis = visible_count(pos[t], ratio, n_comp[t], &flags);
+    const int64_t row0 = seq_kv[t];
+    if (row0 < 0) {
+      flags |= CSA_DERR_BAD_META;
+      n_vis = 0;
+    } else if (row0 + n_vis > k_rows) {
+      flags |= CSA_DERR_KEY_RANGE;
+      n_vis = 0;
+    }
+    if (n_vis > ld) {
+      flags |= CSA_DERR_VIS_OVER_LD;
+      n_vis = ld;
+    }
+    if (blockIdx.x == 0) report(err, flags);
+    s_row0[t] = row0 < 0 ? 0 : row0;
+    s_nvis[t] = (int32_t)n_vis;
+    items = (uint32_t)((n_vis + kTileN * kWaves - 1) / (kTileN * kWaves));
+  }
+  const uint32_t incl = wave_incl_scan_u32(items);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) before += v < wave ? s_wsum[v] : 0u;
+  if (threadIdx.x < T) s_pref[threadIdx.x + 1] = before + incl;
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  __syncthreads();
+  const uint32_t N = s_pref[T];
+  const uint32_t I0 = (uint32_t)(((uint64_t)N * blockIdx.x) / gridDim.x);
+  const uint32_t I1 = (uint32_t)(((uint64_t)N * (blockIdx.x + 1)) / gridDim.x);
+  if (I0 >= I1) return;  // workgroup-uniform
+
+  // the token of item k (items in order: the token only moves forward)
+  int tk = 0;
+  auto token_of = [&](uint32_t k, int from) {
+    int t = from;
+    while (s_pref[t + 1] <= k) ++t;
+    return t;
+  };
+  auto issue_tile = [&](uint32_t k, int b) {
+    const int t = token_of(k, tk);
+    const int64_t n_vis = s_nvis[t];
+    const int64_t tile = (int64_t)(k - s_pref[t]) * kWaves + wave;
+    const char* kbase = reinterpret_cast<const char*>(k_idx + s_row0[t] * IHD);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int e = i * 64 + lane;
+      const int r = e / CPR;
+      const int p = e % CPR;
+      const int c = p ^ (r & (CPR - 1));
+      int64_t blk = tile * kTileN + r;
+      if (blk > n_vis - 1) blk = n_vis - 1;  // past the row's end: re-read a valid row
+      lds_dma16(kbase + blk * RB + c * 16, &ktile[wave][b][i * 64]);
+    }
+  };
+  // both first tiles before the first query load
+  issue_tile(I0, 0);
+  if (I0 + 1 < I1) issue_tile(I0 + 1, 1);
+
+  float wv[MT][16];
+  int cur_t = -1;
+  // An item's results are stored one iteration later, after the wait for
+  // the next tile, so that the wait never covers stores just issued.
+  struct Pending {
+    bool ok = false, store = false;
+    int t = 0;
+    int64_t tile = 0, blk = 0;
+    float part = 0.f;
+    uint64_t val = 0ull;
+    uint32_t n_ok = 0;
+  } pd;
+  auto flush = [&]() {
+    if (!pd.ok) return;  // wave-uniform
+    if (pd.store) scores[(int64_t)pd.t * ld + pd.blk] = pd.part;
+    if (ca.cand != nullptr) cand_publish(pd.val, pd.n_ok, ca, pd.t, pd.tile, 0, nullptr, 0);
+    pd.ok = false;
+  };
+  tk = token_of(I0, 0);
+  for (uint32_t k = I0; k < I1; ++k) {
+    const int t = token_of(k, tk);
+    tk = t;
+    const int b = (int)((k - I0) & 1u);
+    if (t != cur_t) {  // workgroup-uniform: drain, then this token's queries and weights
+      wait_vmcnt<0>();
+      __syncthreads();  // every wave is done with the previous query block
+      const uint16_t* qt = q_idx + (int64_t)t * n_ih * IHD;
+#pragma unroll
+      for (int e0 = 0; e0 < QCHUNKS; e0 += kWaves * 64) {
+        const int e = e0 + wave * 64 + lane;
+        if (e0 + wave * 64 < QCHUNKS) {  // wave-uniform
+          const int r = e / CPR, pp = e % CPR;
+          const int hq = r < n_ih ? r : n_ih - 1;
+          lds_dma16(reinterpret_cast<const char*>(qt) + (int64_t)hq * RB + (pp ^ (r & (CPR - 1))) * 16,
+                    &qlds[e0 + wave * 64]);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float x = w[(int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1)];
+          wv[mt][r] = hw < n_ih ? x : 0.0f;
+        }
+      }
+      wait_vmcnt<0>();
+      __syncthreads();  // the query block is in LDS for every wave
+      cur_t = t;
+    }
+    // all but the next item's tile DMA (if issued) have landed: vector
+    // memory operations complete in order, and the stores issued since that
+    // DMA are the previous item's, issued an iteration ago
+    if (k + 1 < I1) wait_vmcnt<LPT>(); else wait_vmcnt<0>();
+    u32x4 kb[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const int c = 2 * s2 + half;
+      kb[s2] = ktile[wave][b][col * CPR + (c ^ (col & (CPR - 1)))];
+    }
+    wait_lgkmcnt0();  // buffer b is free again
+    flush();          // the previous item's scores and list
+    if (k + 2 < I1) issue_tile(k + 2, b);
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+    // query operands from LDS at each k-step (the registers go to the
+    // pipeline and the deferred results)
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = mt * 32 + col;
+        const int c = 2 * s2 + half;
+        const u32x4 qa = qlds[r * CPR + (c ^ (r & (CPR - 1)))];
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa),
+                                                          __builtin_bit_cast(bf16x8, kb[s2]),
+                                                          acc[mt], 0, 0, 0);
+      }
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+    }
+    part += __shfl_xor(part, 32);
+
+    const int64_t n_vis = s_nvis[t];
+    const int64_t tile = (int64_t)(k - s_pref[t]) * kWaves + wave;
+    const int64_t blk = tile * kTileN + col;
+    pd.ok = tile * kTileN < n_vis;  // wave-uniform
+    pd.t = t;
+    pd.tile = tile;
+    pd.part = part;
+    pd.store = half == 0 && blk < n_vis;
+    pd.blk = blk;
+    if (ca.cand != nullptr && pd.ok) {
+      // the tile's top-m keys in lanes 0..m-1, descending (its group's list)
+      const bool tv = half == 1 && blk < n_vis;
+      const uint32_t tsk = tv ? score_key(part) : 0u;
+      const uint64_t tkey = tsk != 0u ? ((uint64_t)tsk << 32) | (uint32_t)~(uint32_t)blk : 0ull;
+      uint32_t rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) rank += readlane_u64(tkey, 32 + j) > tkey ? 1u : 0u;
+      const uint32_t nnz = (uint32_t)__popcll(__ballot(tkey != 0ull));
+      const int addr = (int)(min(rank, 63u) * 4u);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)(tkey >> 32));
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)tkey);
+      const uint64_t got = ((uint64_t)hi << 32) | lo;
+      pd.val = lane < ca.wave_m && (uint32_t)lane < nnz ? got : 0ull;
+      pd.n_ok = (uint32_t)__popcll(__ballot(tv));
+    }
+  }
+  flush();
+}
+
 template <int IHD, int MT>
 hipError_t launch_t(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t s) {
   dim3 grid(p.wgs_per_token, a.T);
@@ -464,6 +683,25 @@ hipError_t launch_rescore_ihd(const RescoreLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int IHD>
+hipError_t launch_batch_ihd(const IndexScoreLaunch& a, hipStream_t s) {
+  const uint16_t* q = static_cast<const uint16_t*>(a.q_idx);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k_idx);
+  if (a.n_ih <= 32)
+    hipLaunchKernelGGL((index_batch_kernel<IHD, 1>), dim3(kBatchGrid), dim3(kWaves * 64), 0, s, q,
+                       a.w, k, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.T, a.n_ih, a.ratio, a.scores,
+                       a.ld, a.cand, a.err);
+  else
+    hipLaunchKernelGGL((index_batch_kernel<IHD, 2>), dim3(kBatchGrid), dim3(kWaves * 64), 0, s, q,
+                       a.w, k, a.k_rows, a.pos, a.seq_kv, a.n_comp, a.T, a.n_ih, a.ratio, a.scores,
+                       a.ld, a.cand, a.err);
+  return hipGetLastError();
+}
+
+bool batch_indexer(int T, int n_ih, int ihd, int e4m3) {
+  return T > 1 && T <= kBatchMaxT && n_ih <= 64 && !e4m3 && (ihd == 64 || ihd == 128);
+}
+
 }  // namespace
 
 IndexPlan plan_index(int T, int64_t ld) {
@@ -475,11 +713,14 @@ IndexPlan plan_index(int T, int64_t ld) {
   const int64_t total = tiles * (T > 0 ? T : 1);
   int64_t tpw = (total + kWaves * 256 - 1) / (kWaves * 256);
   if (tpw < 1) tpw = 1;
-  // A batch of rows of different lengths is planned for its longest; half
-  // the tiles per wave then keeps the workgroups of the longer rows from
-  // running alone at the end (large prefill chunks keep the full length).
-  const int cap = T > 1 && T <= 512 ? kMaxTpw / 2 : kMaxTpw;
-  if (tpw > cap) tpw = cap;
+  // A batch of rows of different lengths is planned for its longest.  Up to
+  // 2048 tiles a row (the select holds that many group bounds), a batch has
+  // one tile per wave: the geometry of index_batch_kernel's items.  Longer
+  // rows in a batch take half the tiles per wave, so that the workgroups of
+  // the longer rows do not run alone at the end (large prefill chunks keep
+  // the full length).
+  if (T > 1 && T <= kBatchMaxT) tpw = tiles <= kMaxGroups ? 1 : (tpw < kMaxTpw / 2 ? tpw : kMaxTpw / 2);
+  if (tpw > kMaxTpw) tpw = kMaxTpw;
   p.tiles_per_wave = (int)tpw;
   p.wgs_per_token = (int)((tiles + kWaves * tpw - 1) / (kWaves * tpw));
   return p;
@@ -487,7 +728,12 @@ IndexPlan plan_index(int T, int64_t ld) {
 
 hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const IndexPlan p = plan_index(a.T, a.ld);
+  const IndexPlan bp = plan_index(a.T, a.ld);
+  if (batch_indexer(a.T, a.n_ih, a.ihd, a.e4m3) && bp.tiles_per_wave == 1 &&
+      (a.cand.cand == nullptr || !a.cand.merge)) {
+    return a.ihd == 64 ? launch_batch_ihd<64>(a, s) : launch_batch_ihd<128>(a, s);
+  }
+  const IndexPlan& p = bp;
   switch (a.ihd) {
     case 32: return launch_ihd<32>(a, p, s);
     case 64: return launch_ihd<64>(a, p, s);
