@@ -718,8 +718,10 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
 //      atomics);
 //   3. wave 0 reads the histogram (lane l takes the 16-byte groups q*64 + l,
 //      conflict-free) and finds the threshold bin with four DPP scans;
-//   4. each wave lists its keys of that bin in its own LDS region; wave 0
-//      ranks them with lane reads and takes the k-th key;
+//   4. the keys of that bin go to one LDS array (one LDS atomic per wave
+//      places each wave's run), and each 16-lane row ranks one of them: its
+//      lanes count the larger keys among four slots apiece, the row sums the
+//      counts, and the key of rank need - 1 is the threshold;
 //   5. each thread checks its group bounds against it and counts its
 //      selected keys, and one exchange gives each thread its first output
 //      position.
@@ -728,6 +730,16 @@ __device__ __forceinline__ SelResult select_token(const float* __restrict__ srow
 // when all keys share one score value, or when the threshold bin is crowded;
 // the caller then runs select_token, which handles every case.  Lane reads
 // (readlane, ballot) are all made where every lane of the wave is active.
+// Sum over each 16-lane row, in every lane of the row: DPP quad swaps, then
+// the half-row and row mirrors.
+__device__ __forceinline__ uint32_t row_sum16_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // half-row mirror
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);  // row mirror
+  return v;
+}
+
 constexpr int kFastBins = 1024;
 constexpr int kFastQ = kFastBins / 256;  // 16-byte histogram groups per lane
 constexpr int kFastBinCap = 64;
@@ -735,8 +747,9 @@ template <int NT>
 struct FastShared {
   static constexpr int W = NT / 64;
   uint32_t hist[kFastBins];
-  uint64_t wb[W][kFastBinCap];  // each wave's keys of the threshold bin
-  uint32_t wmin[W], wmax[W], wn[W], wsel[W], wflag[W];
+  uint64_t bk[kFastBinCap];  // the keys of the threshold bin, in no order
+  uint32_t nb;               // keys placed in bk so far
+  uint32_t wmin[W], wmax[W], wsel[W], wflag[W];
   uint32_t bin, need, in_bin, total;  // wave 0's verdict on the histogram
   uint64_t thr;                       // wave 0's k-th key
 };
@@ -749,6 +762,7 @@ __device__ __forceinline__ bool fast_select(const uint64_t (&key)[KP], const uin
                                             uint32_t k, FastShared<NT>& sh, int32_t* dst,
                                             uint32_t e_lo, uint32_t e_hi, uint32_t* emitted) {
   constexpr int W = NT / 64;
+  static_assert(W * 4 == kFastBinCap, "step 4 ranks four keys per wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // ---- 1. range; clear the histogram ----
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -759,6 +773,7 @@ __device__ __forceinline__ bool fast_select(const uint64_t (&key)[KP], const uin
     hi = max(hi, h);
   }
   for (int b = tid; b < kFastBins; b += NT) sh.hist[b] = 0u;
+  if (tid == 0) sh.nb = 0u;
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
   if (lane == 0) {
@@ -903,39 +918,40 @@ __device__ __forceinline__ bool fast_select(const uint64_t (&key)[KP], const uin
       return false;
     }
   }
-  // ---- 4. the bin's keys, each wave's in its own region; wave 0 ranks ----
-  uint32_t woff = 0;
+  // ---- 4. the bin's keys (in_bin <= kFastBinCap of them) into bk, then
+  // row r of wave w ranks key 4w + r: lane c of the row counts the larger
+  // keys among slots 4c .. 4c+3 (keys are unique), and the row's sum is the
+  // key's rank ----
+  uint64_t bm[KP];
+  uint32_t wcnt = 0;
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
-    const bool inb = in_play(key[i]) && bin_of(key[i]) == b;
-    const uint64_t m = __ballot(inb);
-    if (inb) sh.wb[wave][woff + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = key[i];
-    woff += (uint32_t)__popcll(m);
+    bm[i] = __ballot(in_play(key[i]) && bin_of(key[i]) == b);
+    wcnt += (uint32_t)__popcll(bm[i]);
   }
-  if (lane == 0) sh.wn[wave] = woff;
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t wn = lane < W ? sh.wn[lane] : 0u;
-    const uint32_t wpre = wave_incl_scan_u32(wn) - wn;
-    // lane j takes the j-th key of the waves' lists laid end to end: one LDS
-    // read from a region and offset found with scalar compares
-    uint32_t src_w = 0, src_o = 0;
+  if (wcnt != 0u) {  // wave-uniform
+    uint32_t o = 0;
+    if (lane == 0) o = atomicAdd(&sh.nb, wcnt);
+    o = (uint32_t)__builtin_amdgcn_readfirstlane((int)o);
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane((int)wpre, w);
-      const uint32_t n0 = (uint32_t)__builtin_amdgcn_readlane((int)wn, w);
-      if ((uint32_t)lane >= p0 && (uint32_t)lane < p0 + n0) {
-        src_w = (uint32_t)w;
-        src_o = (uint32_t)lane - p0;
-      }
+    for (int i = 0; i < KP; ++i) {
+      if ((bm[i] >> lane) & 1ull) sh.bk[o + (uint32_t)__popcll(bm[i] & ((1ull << lane) - 1ull))] = key[i];
+      o += (uint32_t)__popcll(bm[i]);
     }
-    const uint64_t got = sh.wb[src_w][src_o];
-    const uint64_t mine = (uint32_t)lane < in_bin ? got : 0ull;
+  }
+  __syncthreads();
+  {
+    const uint32_t j = 4u * (uint32_t)wave + (uint32_t)(lane >> 4);
+    const uint32_t m0 = 4u * (uint32_t)(lane & 15);
+    const uint64_t kj = j < in_bin ? sh.bk[j] : 0ull;
     uint32_t gt = 0;
-    for (uint32_t m = 0; m < in_bin; ++m) gt += readlane_u64(mine, (int)m) > mine ? 1u : 0u;
-    const uint64_t tm = __ballot((uint32_t)lane < in_bin && gt == need - 1u);
-    const uint64_t t = readlane_u64(mine, __ffsll((unsigned long long)tm) - 1);
-    if (lane == 0) sh.thr = t;
+#pragma unroll
+    for (uint32_t e = 0; e < 4u; ++e) {
+      const uint64_t km = m0 + e < in_bin ? sh.bk[m0 + e] : 0ull;
+      gt += km > kj ? 1u : 0u;
+    }
+    gt = row_sum16_u32(gt);
+    if ((lane & 15) == 0 && j < in_bin && gt == need - 1u) sh.thr = kj;
   }
   __syncthreads();
   // ---- 5. group bounds and output positions ----
