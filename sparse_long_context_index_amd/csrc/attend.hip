@@ -637,111 +637,110 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
 
 // Merge of the split partials of one (token, head): out = sum_s w_s o_s with
 // w_s = l_s e^{m_s - M} / (sum_s' l_s' e^{m_s' - M} [+ e^{sink - M}]), where
-// o_s is split s's normalised bf16 output.  Wave w takes splits w, w+4, ...;
-// the first eight of each wave are loaded together with every split's (max,
-// sum), so up to 32 splits cost one memory round trip.
+// o_s is split s's normalised bf16 output.  A workgroup is one wave per 256
+// output elements of the head (two waves at head_dim 512), and the waves
+// share nothing: each reads every split's (max, sum) -- lane l takes splits
+// l, l + 64, ... -- and reduces them with DPP, then its part of every split's
+// output in rounds of kCombCh splits, all of a round's loads in flight
+// together.  No LDS, no barrier.
+constexpr int kCombCh = 32;
 template <int D>
-__global__ __launch_bounds__(256) void attend_combine_kernel(AttendLaunch p, int n_splits) {
-  constexpr int EPL = D / 64;  // output elements per lane
-  constexpr int SG = 4;        // split groups = waves
-  constexpr int CH = 8;        // splits per group per round
-  __shared__ float fw[kMaxSplits];
-  __shared__ float wred[2][SG];
-  __shared__ __attribute__((aligned(16))) float red[SG][D];
-  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+constexpr int comb_waves() { return D >= 512 ? D / 256 : 1; }
+template <int EPL> struct CombRaw;
+template <> struct CombRaw<4> { using T = uint2; };
+template <> struct CombRaw<2> { using T = uint32_t; };
+template <> struct CombRaw<1> { using T = uint16_t; };
+template <int EPL>
+__device__ __forceinline__ float comb_elem(const typename CombRaw<EPL>::T& r, int j) {
+  if constexpr (EPL == 4) {
+    const uint32_t w = j < 2 ? r.x : r.y;
+    return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  } else if constexpr (EPL == 2) {
+    return __uint_as_float((j & 1) ? (r & 0xFFFF0000u) : (r << 16));
+  } else {
+    return __uint_as_float((uint32_t)r << 16);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * comb_waves<D>()) void attend_combine_kernel(AttendLaunch p, int n_splits) {
+  constexpr int NW = comb_waves<D>();
+  constexpr int EPL = D / (64 * NW);  // output elements per lane
+  constexpr int MLR = kMaxSplits / 64;
+  using Raw = typename CombRaw<EPL>::T;
+  const int h = blockIdx.x, t = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* part_ml = static_cast<const float*>(p.ws);
   const uint16_t* part_o =
       reinterpret_cast<const uint16_t*>(part_ml + part_ml_floats(p.T, n_splits, p.n_heads));
   const size_t slot0 = (size_t)t * n_splits * p.n_heads + h;
   const size_t sstride = (size_t)p.n_heads * D;
-  const uint16_t* pbase = part_o + slot0 * D + lane * EPL;
+  const int e0 = wave * (D / NW) + lane * EPL;  // this lane's first output element
+  const uint16_t* pbase = part_o + slot0 * D + e0;
 
-  // Every load is unconditional (split index clamped, value masked after):
-  // a load inside `if (s < n_splits)` waits for its data before the branch
-  // closes, which chained the round's loads one round trip after another.
-  float m_s, l_s;
-  {
-    const size_t slot = slot0 + (size_t)min(tid, n_splits - 1) * p.n_heads;
-    const float2 ml = *reinterpret_cast<const float2*>(part_ml + slot * 2);
-    m_s = tid < n_splits ? ml.x : -INFINITY;
-    l_s = tid < n_splits ? ml.y : 0.f;
+  // Every load is unconditional (split index clamped, value masked after): a
+  // load under a per-lane branch waits for its data before the branch closes.
+  float m_s[MLR], l_s[MLR];
+#pragma unroll
+  for (int r = 0; r < MLR; ++r) {
+    const int s = lane + 64 * r;
+    const float2 ml = *reinterpret_cast<const float2*>(
+        part_ml + (slot0 + (size_t)min(s, n_splits - 1) * p.n_heads) * 2);
+    m_s[r] = s < n_splits ? ml.x : -INFINITY;
+    l_s[r] = s < n_splits ? ml.y : 0.f;
   }
-  float v[CH][EPL];
+  Raw raw[kCombCh];
   auto load_round = [&](int c0) {
-    constexpr int NQ = EPL % 8 == 0 ? EPL / 8 : 1;
-    u32x4 raw[CH][NQ];
-    uint16_t raw1[CH][EPL % 8 == 0 ? 1 : EPL];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int s = min(wave + SG * (c0 + c), n_splits - 1);
-      const uint16_t* src = pbase + (size_t)s * sstride;
-      if constexpr (EPL % 8 == 0) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) raw[c][q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
-      } else {
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) raw1[c][j] = src[j];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const bool ok = wave + SG * (c0 + c) < n_splits;
-      if constexpr (EPL % 8 == 0) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[c][8 * q + 2 * e] = ok ? __uint_as_float(raw[c][q][e] << 16) : 0.f;
-            v[c][8 * q + 2 * e + 1] = ok ? __uint_as_float(raw[c][q][e] & 0xFFFF0000u) : 0.f;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) v[c][j] = ok ? bf16_to_f32(raw1[c][j]) : 0.f;
-      }
-    }
+    for (int c = 0; c < kCombCh; ++c)
+      raw[c] = *reinterpret_cast<const Raw*>(pbase + (size_t)min(c0 + c, n_splits - 1) * sstride);
   };
   load_round(0);
 
-  float M = wave_max_f32(l_s > 0.f ? m_s : -INFINITY);
-  if (lane == 0) wred[0][wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < MLR; ++r) mx = fmaxf(mx, l_s[r] > 0.f ? m_s[r] : -INFINITY);
+  float M = wave_max_f32(mx);
   float s2 = -INFINITY;
   if (p.sink != nullptr) {
     s2 = p.sink[h] * kLog2e;
     M = fmaxf(M, s2);
   }
-  const float f = (l_s > 0.f) ? l_s * exp2f(m_s - M) : 0.f;
-  fw[tid] = f;
-  const float Lp = wave_sum_f32(f);
-  if (lane == 0) wred[1][wave] = Lp;
-  __syncthreads();
-  float Lsum = wred[1][0] + wred[1][1] + wred[1][2] + wred[1][3];
+  float f[MLR];
+  float fs = 0.f;
+#pragma unroll
+  for (int r = 0; r < MLR; ++r) {
+    f[r] = l_s[r] > 0.f ? l_s[r] * exp2f(m_s[r] - M) : 0.f;
+    fs += f[r];
+  }
+  float Lsum = wave_sum_f32(fs);
   if (p.sink != nullptr) Lsum += exp2f(s2 - M);
 
   float acc[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) acc[j] = 0.f;
-  for (int c0 = 0; wave + SG * c0 < n_splits; c0 += CH) {
+  for (int c0 = 0; c0 < n_splits; c0 += kCombCh) {
     if (c0 > 0) load_round(c0);
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int s = wave + SG * (c0 + c);
-      const float wgt = s < n_splits ? fw[s] : 0.f;
+    for (int c = 0; c < kCombCh; ++c) {
+      const int s = c0 + c;
+      if (s < n_splits) {  // wave-uniform
+        // split s's weight sits in lane s % 64 of f[s / 64]
+        const int r = s >> 6;
+        float fr = f[0];
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[j] += wgt * v[c][j];
+        for (int rr = 1; rr < MLR; ++rr) fr = r == rr ? f[rr] : fr;
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fr), s & 63));
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) acc[j] += w * comb_elem<EPL>(raw[c], j);
+      }
     }
   }
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) red[wave][lane * EPL + j] = acc[j];
-  __syncthreads();
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  uint16_t* oh = p.out + ((size_t)t * p.n_heads + h) * D;
-  for (int e = tid; e < D; e += 256)
-    oh[e] = f32_to_bf16((red[0][e] + red[1][e] + red[2][e] + red[3][e]) * inv);
-  if (p.lse != nullptr && tid == 0)
+  uint16_t* oh = p.out + ((size_t)t * p.n_heads + h) * D + e0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) oh[j] = f32_to_bf16(acc[j] * inv);
+  if (p.lse != nullptr && threadIdx.x == 0)
     p.lse[(size_t)t * p.n_heads + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
@@ -796,7 +795,7 @@ hipError_t launch_d(const AttendLaunch& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.n_splits == 1) return e;
   hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),
-                     dim3(256), 0, s, a, sp.n_splits);
+                     dim3(64 * comb_waves<D>()), 0, s, a, sp.n_splits);
   return hipGetLastError();
 }
 
@@ -822,7 +821,7 @@ hipError_t launch_fused_d(const SelectLaunch& sl, const AttendLaunch& a, hipStre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.n_splits == 1) return e;
   hipLaunchKernelGGL((attend_combine_kernel<D>), dim3((unsigned)a.n_heads, (unsigned)a.T),
-                     dim3(256), 0, s, a, sp.n_splits);
+                     dim3(64 * comb_waves<D>()), 0, s, a, sp.n_splits);
   return hipGetLastError();
 }
 

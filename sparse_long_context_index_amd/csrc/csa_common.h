@@ -243,10 +243,11 @@ struct CandArgs {
 // last, so that the select can list its selection in block order from slot
 // positions.  Without merging the list is its group's list and the
 // group bound is the list's last key when the wave has more valid blocks.
-// With merging every wave of the workgroup calls this (it holds a barrier):
-// each wave's list and bound go to LDS (wave w's kMergeMaxWaveM + 1 words at
-// lds + w*lds_stride, lds_stride >= kMergeScratch), and wave 0 keeps the
-// list_len largest of those kIndexWaves*wave_m keys.  A block missing from the merged list is either
+// With merging every wave of the workgroup calls this (it holds two
+// barriers): each wave's list and bound go to LDS (wave w's kMergeMaxWaveM + 1
+// words at lds + w*lds_stride, lds_stride >= kMergeScratch); every wave ranks
+// its own keys among all kIndexWaves*kMergeMaxWaveM of them, and the keys of
+// rank below list_len go to LDS by rank, from where wave 0 stores them.  A block missing from the merged list is either
 // below the largest key left out of it, or missing from its wave's list and
 // so below that wave's last key; the bound is the larger of those.
 __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const CandArgs& ca,
@@ -269,40 +270,45 @@ __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const 
     if (lane == 0) ca.gcut[g] = wbound;
     return;
   }
+  static_assert(kIndexWaves == 8 && kMergeMaxWaveM == 8, "one 8-lane group per listed key");
   uint64_t* mine = lds + wave * lds_stride;
+  uint64_t* tmp = lds + kMergedLen;                // wave 0's region past its list: kept keys by rank
+  uint64_t* cut_slot = lds + kMergeMaxWaveM + 1;   // ... and the largest key left out
   if (lane < kMergeMaxWaveM) mine[lane] = lane < m ? val : 0ull;
   if (lane == 0) mine[kMergeMaxWaveM] = wbound;
+  if (wave == 0 && lane == 0) *cut_slot = 0ull;
+  __syncthreads();
+  // Key e = lane / 8 of this wave's list: lane c = lane % 8 of its 8-lane
+  // group counts the larger keys (and the nonzero keys) among wave c's
+  // slots; the group's sums are the key's rank (keys are unique where
+  // nonzero) and the number of nonzero keys in all the lists.
+  const uint64_t key = mine[lane >> 3];
+  const uint64_t* other = lds + (lane & 7) * lds_stride;
+  uint32_t above = 0, nz = 0;
+#pragma unroll
+  for (int e = 0; e < kMergeMaxWaveM; ++e) {
+    const uint64_t o = other[e];
+    above += o > key ? 1u : 0u;
+    nz += o != 0ull ? 1u : 0u;
+  }
+  above += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)above, 0xB1, 0xF, 0xF, false);  // quad [1,0,3,2]
+  above += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)above, 0x4E, 0xF, 0xF, false);  // quad [2,3,0,1]
+  above += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)above, 0x141, 0xF, 0xF, false); // half-row mirror
+  nz += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nz, 0xB1, 0xF, 0xF, false);
+  nz += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nz, 0x4E, 0xF, 0xF, false);
+  nz += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nz, 0x141, 0xF, 0xF, false);
+  if ((lane & 7) == 0 && key != 0ull) {
+    if (above < (uint32_t)ca.list_len) tmp[above] = key;
+    else if (above == (uint32_t)ca.list_len) *cut_slot = key;
+  }
   __syncthreads();
   if (wave != 0) return;
-  const int w = lane / m;
-  const uint64_t key = lane < kIndexWaves * m ? lds[w * lds_stride + (lane - w * m)] : 0ull;
-  // Rank among the kIndexWaves*m keys (unique where nonzero): the number of
-  // larger keys, read back from LDS by every lane at once (broadcast reads
-  // of every slot; unused slots hold zero); zero keys rank after all nonzero
-  // keys in lane order.
-  uint32_t above = 0;
-#pragma unroll 1
-  for (int v0 = 0; v0 < kIndexWaves; v0 += 2) {  // two waves' slots per batch of reads
-    uint64_t kv[2 * kMergeMaxWaveM];
-#pragma unroll
-    for (int j = 0; j < 2 * kMergeMaxWaveM; ++j)
-      kv[j] = lds[(v0 + j / kMergeMaxWaveM) * lds_stride + j % kMergeMaxWaveM];
-#pragma unroll
-    for (int j = 0; j < 2 * kMergeMaxWaveM; ++j) above += kv[j] > key ? 1u : 0u;
-  }
-  const uint64_t zero_lanes = __ballot(key == 0ull);
-  const uint32_t nonzero = 64u - (uint32_t)__popcll(zero_lanes);
-  const uint32_t rank =
-      key != 0ull ? above
-                  : nonzero + (uint32_t)__popcll(zero_lanes & ((1ull << lane) - 1ull));
   const int64_t g = t * ca.groups_per_token + wg_in_token;
-  // the list_len largest keys, in key order, into LDS scratch; then each list
-  // slot takes its block-order position among them
-  uint64_t* tmp = lds + kMergedLen;  // wave 0's region past its own list
-  if (rank < (uint32_t)ca.list_len) tmp[rank] = key;
-  const uint32_t nnz_l = min(nonzero, (uint32_t)ca.list_len);
+  // the kept keys in key order are tmp[0 .. nnz_l); each list slot takes its
+  // block-order position among them, zero keys last
+  const uint32_t nnz_l = min(nz, (uint32_t)ca.list_len);
   if (lane < ca.list_len) {
-    const uint64_t kl = tmp[lane];
+    const uint64_t kl = (uint32_t)lane < nnz_l ? tmp[lane] : 0ull;
     const uint32_t bl = ~(uint32_t)kl;
     uint32_t pos = (uint32_t)lane;
     if ((uint32_t)lane < nnz_l) {
@@ -312,8 +318,7 @@ __device__ __forceinline__ void cand_publish(uint64_t val, uint32_t n_ok, const 
     ca.cand[g * ca.list_len + pos] = kl;
   }
   // the largest key left out of the list, and the waves' own bounds
-  const uint64_t out_mask = __ballot(rank == (uint32_t)ca.list_len);
-  uint64_t cut = out_mask != 0ull ? readlane_u64(key, __ffsll((unsigned long long)out_mask) - 1) : 0ull;
+  uint64_t cut = *cut_slot;
 #pragma unroll
   for (int v = 0; v < kIndexWaves; ++v) {
     const uint64_t wc = lds[v * lds_stride + kMergeMaxWaveM];
