@@ -60,6 +60,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// The group of tiles of workgroup L among G.  The dispatcher deals
+// workgroups to the eight XCDs in turn (L % 8), so with groups in workgroup
+// order XCD x would read only groups x, x + 8, ...: one fixed eighth of every
+// eight consecutive groups (at 1M, of every 2 MiB of keys), at a rate that was
+// measured to differ from XCD to XCD by up to a fifth.  The diagonal order
+// gives XCD x the groups 8k + (x + k) % 8 instead, every position equally
+// often.
+__device__ __forceinline__ int index_group(int L, int G) {
+  return (G & 7) == 0 ? (L & ~7) | (((L & 7) + (L >> 3)) & 7) : L;
+}
+
 // Up to 64 indexer heads the register budget is held to two waves per SIMD;
 // more heads need more registers and run one wave per SIMD.
 //
@@ -169,9 +180,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   }
 
   const int64_t n_tiles = (n_vis + kTileN - 1) / kTileN;
-  const int64_t tile_begin = ((int64_t)blockIdx.x * kWaves + wave) * tiles_per_wave;
+  const int grp = index_group((int)blockIdx.x, (int)gridDim.x);
+  const int64_t tile_begin = ((int64_t)grp * kWaves + wave) * tiles_per_wave;
   const int64_t tile_end = min(tile_begin + (int64_t)tiles_per_wave, n_tiles);
-  const int64_t wave_in_token = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t wave_in_token = (int64_t)grp * kWaves + wave;
   const bool active = tile_begin < tile_end;  // wave-uniform
   const char* kbase = reinterpret_cast<const char*>(k_idx + row0 * RB);
 
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   static_assert(kCandStride >= kMergeScratch, "merge scratch fits a wave's buffers");
   if (!active) {
     if (ca.cand != nullptr)  // empty list and bound (and the merge barrier)
-      cand_publish(0ull, 0u, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
+      cand_publish(0ull, 0u, ca, t, wave_in_token, grp, cand_lds, kCandStride);
     return;
   }
   Op qv[kQRegs ? MT : 1][KS];
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   }
 
   if (ca.cand != nullptr)
-    cand_publish(rl, n_ok, ca, t, wave_in_token, blockIdx.x, cand_lds, kCandStride);
+    cand_publish(rl, n_ok, ca, t, wave_in_token, grp, cand_lds, kCandStride);
 }
 
 // Batches of 2..kBatchMaxT rows: a persistent grid of one workgroup per CU
