@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
   const int64_t row0 = seq_kv[t];
   asm volatile("" ::"s"(pos_t), "s"(ncomp_t), "s"(row0), "s"(k_rows), "s"(ld), "s"(ratio),
                "s"(tiles_per_wave), "s"(n_ih));
-  wait_vmcnt<0>();  // query DMA and weight loads have landed
+  // The first key tiles need only this metadata: they are issued before the
+  // query block and head weights are waited for (below).
 
   uint32_t flags = 0;
   int64_t n_vis = visible_count(pos_t, ratio, ncomp_t, &flags);
@@ -170,14 +171,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
     n_vis = ld;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) report(err, flags);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (hw >= n_ih) wv[mt][r] = 0.0f;
-    }
-  }
 
   const int64_t n_tiles = (n_vis + kTileN - 1) / kTileN;
   const int grp = index_group((int)blockIdx.x, (int)gridDim.x);
@@ -216,9 +209,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       }
     }
   }
-  if (active) {
-    issue_tile(tile_begin, 0);
-    if (tile_begin + 1 < tile_end) issue_tile(tile_begin + 1, 1);
+  const int n_first = active ? (tile_begin + 1 < tile_end ? 2 : 1) : 0;  // wave-uniform
+  if (n_first > 0) issue_tile(tile_begin, 0);
+  if (n_first > 1) issue_tile(tile_begin + 1, 1);
+  // the query DMA and the weight loads, issued before the tiles, have landed
+  if (n_first == 2) wait_vmcnt<2 * LPT>();
+  else if (n_first == 1) wait_vmcnt<LPT>();
+  else wait_vmcnt<0>();
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (hw >= n_ih) wv[mt][r] = 0.0f;
+    }
   }
   __syncthreads();  // the query block is in LDS for every wave
   // After its last tile each wave's own tile buffers hold its candidate list
