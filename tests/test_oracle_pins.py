@@ -322,3 +322,72 @@ def test_tiny_end_to_end_shapes():
     r = csa_token(inp, 0)
     assert r["n_vis"] == 63 and len(r["sel"]) == 16 and r["rows"].shape == (32, 64)
     assert r["out"].shape == (8, 64) and np.isfinite(r["lse"]).all()
+
+
+def _unpacked_token(inp, t):
+    """Token t of a packed batch rebuilt as a batch of its own: only its own
+    sequence's key and row caches and its own SWA rows, every offset zero."""
+    import dataclasses
+    row0, n = int(inp.seq_kv[t]), int(inp.n_comp[t])
+    s0, sl = int(inp.swa_row0[t]), int(inp.swa_len[t])
+    return dataclasses.replace(
+        inp, q_idx=inp.q_idx[t:t + 1], w=inp.w[t:t + 1], q=inp.q[t:t + 1],
+        k_idx=inp.k_idx[row0:row0 + n].copy(), comp_kv=inp.comp_kv[row0:row0 + n].copy(),
+        swa=inp.swa[s0:s0 + sl].copy(), pos=inp.pos[t:t + 1].copy(),
+        seq_kv=np.zeros(1, np.int64), n_comp=inp.n_comp[t:t + 1].copy(),
+        swa_row0=np.zeros(1, np.int64), swa_len=inp.swa_len[t:t + 1].copy(), planted=None)
+
+
+def test_csa_token_packed_offsets_match_the_token_alone():
+    """Packed batches (1M-context audit, D3/D5: each sequence's compressed rows
+    and its sliding window are its own): a token whose key and row caches
+    start at seq_kv > 0 and whose SWA rows start at swa_row0 > 0 selects and
+    attends exactly as the same token with only its own caches.  The three
+    sequences' caches are drawn independently, so an offset slip reads
+    another sequence's rows; the negative control shifts seq_kv by one row."""
+    inp = gen.synth(31, pos=[201, 333, 250], seq_of_token=[0, 1, 2], n_comp_seq=[50, 83, 62],
+                    n_ih=8, ihd=32, ratio=4, top_k=24, window=16, n_heads=8, head_dim=64,
+                    w_std=0.35)
+    assert inp.seq_kv.tolist() == [0, 50, 133] and inp.swa_row0.tolist() == [0, 16, 32]
+    for t in (1, 2):
+        packed = csa_token(inp, t)
+        alone = csa_token(_unpacked_token(inp, t), 0)
+        assert packed["n_vis"] == alone["n_vis"] == min(int(inp.pos[t]) // 4, int(inp.n_comp[t]))
+        assert packed["sel"].tolist() == alone["sel"].tolist()
+        np.testing.assert_array_equal(packed["rows"], alone["rows"])
+        np.testing.assert_array_equal(packed["out"], alone["out"])
+        np.testing.assert_array_equal(packed["lse"], alone["lse"])
+    shifted = gen.synth(31, pos=[201, 333, 250], seq_of_token=[0, 1, 2], n_comp_seq=[50, 83, 62],
+                        n_ih=8, ihd=32, ratio=4, top_k=24, window=16, n_heads=8, head_dim=64,
+                        w_std=0.35)
+    shifted.seq_kv = shifted.seq_kv + np.array([0, 1, 0])
+    bad = csa_token(shifted, 1)
+    assert not np.allclose(bad["out"], csa_token(inp, 1)["out"])
+
+
+def test_hca_token_over_blocks_enumerated_by_causality():
+    """Dense HCA (1M-context audit, D4) of a query at position pos attends over
+    every stored block that ends before the query's own block begins (PART A,
+    suspect 3), then the SWA rows.  The visible set is enumerated block by
+    block from that definition, and the softmax is written out per head with
+    exp and sums (no max shift at these magnitudes)."""
+    r = np.random.default_rng(41)
+    H, D, window = 4, 32, 8
+    for pos, ratio, n_comp in [(0, 4, 10), (3, 4, 10), (4, 4, 10), (37, 4, 10), (37, 4, 6),
+                               (1000, 128, 9), (1151, 128, 9), (1152, 128, 9)]:
+        comp = gen.f32_to_bf16_bits(r.standard_normal((n_comp + 3, D), dtype=np.float32))
+        swa = gen.f32_to_bf16_bits(r.standard_normal((window, D), dtype=np.float32))
+        q = gen.f32_to_bf16_bits(r.standard_normal((H, D), dtype=np.float32))
+        own_block_start = (pos // ratio) * ratio
+        vis = [b for b in range(n_comp + 3)
+               if b < n_comp and (b + 1) * ratio - 1 < own_block_start]
+        rows = np.concatenate([bf16_to_f64(comp)[vis], bf16_to_f64(swa)], axis=0)
+        qd = bf16_to_f64(q)
+        scale = 1.0 / math.sqrt(D)
+        expect = np.zeros((H, D))
+        for h in range(H):
+            e = np.array([math.exp(scale * float(qd[h] @ rows[j])) for j in range(rows.shape[0])])
+            expect[h] = (e[:, None] * rows).sum(axis=0) / e.sum()
+        o, _ = hca_token(q, comp, visible_blocks(pos, ratio, n_comp), swa, scale)
+        assert visible_blocks(pos, ratio, n_comp) == len(vis)
+        np.testing.assert_allclose(o, expect, rtol=1e-12, atol=1e-13)
