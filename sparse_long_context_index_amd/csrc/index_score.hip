@@ -637,15 +637,19 @@ __global__ __launch_bounds__(256) void rescore_kernel(RescoreLaunch a) {
   if (j0 >= a.C) return;  // wave-uniform
   const int64_t j = j0 + col;
   uint64_t* out = a.key + (int64_t)t * a.C;
+  // one round trip: the count, this lane's candidate slot (clamped into the
+  // C slots), the token's first key row, then (below) its queries and weights
   const int32_t cnt = a.count[t];
+  const int32_t bj = a.idx[(int64_t)t * a.C + (j < a.C ? j : a.C - 1)];
+  const int64_t row0 = a.seq_kv[t];
   if (j0 >= cnt) {  // wave-uniform: no candidate in this tile
     if (half == 0 && j < a.C) out[j] = 0ull;
     return;
   }
-  // lanes past the count re-read the last candidate (a valid row)
+  // lanes past the count take lane 0's candidate (j0 < cnt: a valid row)
   const bool valid = j < cnt;
-  const int32_t b = a.idx[(int64_t)t * a.C + (valid ? j : cnt - 1)];
-  const char* krow = reinterpret_cast<const char*>(a.k_idx) + (a.seq_kv[t] + b) * RB;
+  const int32_t b = valid ? bj : __shfl(bj, 0);
+  const char* krow = reinterpret_cast<const char*>(a.k_idx) + (row0 + b) * RB;
   u32x4 kb[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) kb[s] = *reinterpret_cast<const u32x4*>(krow + (2 * s + half) * 16);
