@@ -226,6 +226,10 @@ def test_gather_bitexact(dev, head_dim):
     (512, 64, [[1152, 0]], False, False),
     (512, 100, [[700, 128], [5, 3]], True, True),
     (512, 64, [[8192, 128]], True, False),
+    # one head group and long rows: 141 and 256 splits (the combine's split
+    # statistics span several slots a lane, its partials several rounds)
+    (128, 16, [[9000, 0]], False, True),
+    (64, 16, [[16384, 0]], False, False),
 ])
 def test_mqa_attend(dev, head_dim, n_heads, lens, two, sink):
     say(f"csa_mqa_attend D={head_dim} H={n_heads} lens={lens} two={two} sink={sink}")
