@@ -356,10 +356,10 @@ def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dic
     import numpy as np
     res = {}
 
-    def csa_config(name, inp, n_layers, replays, e4m3=False, index_stage=False):
+    def csa_config(name, inp, n_layers, replays, e4m3=False, index_stage=False, one_sequence=False):
         layers = layered(inp, n_layers, e4m3=e4m3)
         outs = B.alloc_step_outputs(inp, dev, keep=False, all_kv=False)
-        sargs = [B.step_args(inp, dl, outs, e4m3=e4m3) for dl in layers]
+        sargs = [B.step_args(inp, dl, outs, e4m3=e4m3, one_sequence=one_sequence) for dl in layers]
         ws = B.step_workspace(sargs[0], dev)
         g = R.capture([(lambda a=a: B.csa_decode_step(a, ws)) for a in sargs])
         ms = R.replays(g, n_layers, replays)
@@ -411,7 +411,8 @@ def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dic
     # 4096-token prefill chunk
     log("config: 4096-token prefill chunk")
     inp = gen.prefill()
-    r = csa_config("prefill_4096", inp, 1, 5, index_stage=True)
+    # one sequence: the indexer runs as one GEMM whose key tiles serve eight tokens
+    r = csa_config("prefill_4096", inp, 1, 5, index_stage=True, one_sequence=True)
     flops = 0
     for t in range(inp.T):
         n = min(int(inp.pos[t]) // inp.ratio, int(inp.n_comp[t]))

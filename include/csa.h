@@ -53,7 +53,7 @@ typedef enum csa_status {
 /* Device-side error bits ORed into *err. */
 #define CSA_DERR_VIS_OVER_LD   0x1u  /* n_vis[t] > ld: only the first ld scores kept      */
 #define CSA_DERR_KEY_RANGE     0x2u  /* seq_kv[t]+n_vis[t] > k_rows: token scored as 0 blocks */
-#define CSA_DERR_BAD_META      0x4u  /* pos < 0 or n_comp < 0 or seq_kv < 0              */
+#define CSA_DERR_BAD_META      0x4u  /* pos, n_comp or seq_kv < 0; one_sequence broken    */
 #define CSA_DERR_ROW_RANGE     0x8u  /* gather/attend row outside its buffer: row zeroed / skipped */
 #define CSA_DERR_COUNT_RANGE   0x10u /* count > top_k or swa_len > window: clamped        */
 #define CSA_DERR_ROWS_OVER_MAX 0x20u /* a_len+b_len > max_rows: rows beyond max_rows ignored */
@@ -250,6 +250,13 @@ typedef struct csa_step_args {
   const float* q_idx_scale;
   const uint8_t* k_idx8;
   const float* k_idx_scale;
+  /* 1: every token's key rows start at the same seq_kv (one sequence, e.g. a
+     prefill chunk), which lets S1 score the tokens as one GEMM whose key
+     tiles serve several tokens at once (bf16 indexer, T >= 64).  A token
+     whose seq_kv differs from that of the first token of its group of
+     eight then scores no block and raises CSA_DERR_BAD_META.  0: no
+     assumption.  Other values: CSA_EINVAL. */
+  int one_sequence;
 } csa_step_args;
 
 size_t csa_decode_step_workspace_bytes(const csa_step_args* a);

@@ -48,7 +48,7 @@ class StepArgs(ctypes.Structure):
         ("swa_row0", _vp), ("swa_len", _vp), ("all_kv", _vp), ("out", _vp), ("lse", _vp),
         ("scores", _vp), ("idx", _vp), ("count", _vp), ("n_kv", _vp), ("err", _vp),
         ("idx_e4m3", _i32), ("q_idx8", _vp), ("q_idx_scale", _vp), ("k_idx8", _vp),
-        ("k_idx_scale", _vp),
+        ("k_idx_scale", _vp), ("one_sequence", _i32),
     ]
 
 
@@ -299,10 +299,12 @@ def quantize_indexer_e4m3(d: dict, stream=None) -> dict:
 
 
 def step_args(inp, d: dict, outs: dict, mode: int = CSA_MODE_CSA, max_vis: Optional[int] = None,
-              sink: Optional[torch.Tensor] = None, e4m3: bool = False) -> StepArgs:
+              sink: Optional[torch.Tensor] = None, e4m3: bool = False,
+              one_sequence: bool = False) -> StepArgs:
     """Pack a csa_step_args for a CSAInputs batch whose tensors are in `d`
     (see upload) and whose outputs are in `outs` (all_kv, out, lse, scores,
-    idx, count, n_kv, err; any may be absent)."""
+    idx, count, n_kv, err; any may be absent).  one_sequence: the caller's
+    promise that every token's key rows start at the same seq_kv."""
     a = StepArgs()
     a.mode = mode
     a.T, a.n_ih, a.ihd, a.ratio = inp.T, inp.n_ih, inp.ihd, inp.ratio
@@ -323,6 +325,7 @@ def step_args(inp, d: dict, outs: dict, mode: int = CSA_MODE_CSA, max_vis: Optio
         a.idx_e4m3 = 1
         a.q_idx8, a.k_idx8 = ptr(d["q_idx8"]), ptr(d["k_idx8"])
         a.q_idx_scale, a.k_idx_scale = ptr(d["q_scale"]), ptr(d["k_scale"])
+    a.one_sequence = 1 if one_sequence else 0
     return a
 
 
@@ -347,7 +350,7 @@ def alloc_step_outputs(inp, dev, max_vis: Optional[int] = None, keep=True,
 
 
 def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None, all_kv: bool = True,
-                    e4m3: bool = False) -> dict:
+                    e4m3: bool = False, one_sequence: bool = False) -> dict:
     """Upload a batch, run one csa_decode_step, return host copies (with
     e4m3, the indexer queries and keys are quantised on the GPU first and
     their codes and scales are returned too)."""
@@ -355,7 +358,7 @@ def run_decode_step(inp, dev, sink: Optional[torch.Tensor] = None, all_kv: bool 
     if e4m3:
         d = quantize_indexer_e4m3(d)
     outs = alloc_step_outputs(inp, dev, all_kv=all_kv)
-    a = step_args(inp, d, outs, sink=sink, e4m3=e4m3)
+    a = step_args(inp, d, outs, sink=sink, e4m3=e4m3, one_sequence=one_sequence)
     ws = step_workspace(a, dev)
     csa_decode_step(a, ws)
     torch.cuda.synchronize(dev)

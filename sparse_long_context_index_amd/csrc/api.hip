@@ -11,7 +11,7 @@ using namespace csa;
 
 namespace {
 
-constexpr int kAbiVersion = 2;  // 2: E4M3 indexer entry points and step fields
+constexpr int kAbiVersion = 3;  // 2: E4M3 indexer entry points and step fields; 3: one_sequence
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxGridY = 65535;
 
@@ -178,6 +178,7 @@ csa_status check_step(const csa_step_args* a) {
       !a->swa_row0 || !a->swa_len)
     return CSA_EINVAL;
   if (!isfinite(a->scale)) return CSA_EINVAL;
+  if (a->one_sequence != 0 && a->one_sequence != 1) return CSA_EINVAL;
   if (!aligned16(a->q) || !aligned16(a->comp_kv) || !aligned16(a->swa) || !aligned16(a->out))
     return CSA_EINVAL;
   if (!head_dim_ok(a->head_dim) || a->n_heads > 128 || a->T > kMaxGridY || a->window > 1024)
@@ -389,6 +390,7 @@ csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* str
   }
   I.pos = a->pos; I.seq_kv = a->seq_kv; I.n_comp = a->n_comp;
   I.T = a->T; I.n_ih = a->n_ih; I.ihd = a->ihd; I.ratio = a->ratio;
+  I.one_seq = a->one_sequence;
   I.scores = scores; I.ld = a->max_vis;
   I.cand = cand_args(tp, tw); I.err = a->err;
   hipError_t e = hipSuccess;
@@ -415,6 +417,7 @@ csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* str
   S.cand = tw.cand; S.gcut = tw.gcut; S.list_len = tp.list_len;
   S.groups_per_token = tp.groups_per_token; S.blocks_per_group = tp.blocks_per_group;
   S.idx = idx; S.count = count; S.err = a->err;
+  S.row0_group = gemm_indexer(I) ? kGemmTokens : 0;
   if (a->idx_e4m3) {
     // E4M3 prefilter: the C best blocks by E4M3 score, rescored in bf16; they
     // form one complete candidate list per token for the top-k below

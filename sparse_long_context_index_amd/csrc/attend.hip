@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kFuseThreads) void select_attend_kernel(SelectLaunc
 
   const uint32_t win = (uint32_t)(tiles_per_split * kRT);  // this split's rows
   const sel::SelResult r = sel::step_select<kFuseThreads>(
-      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.seq_kv[t],
+      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, select_row0(sl, t),
       sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
       sl.blocks_per_group, sl.lists_complete != 0, u.f, u.s, selrow, (uint32_t)row_begin,

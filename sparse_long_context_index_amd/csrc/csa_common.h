@@ -342,7 +342,13 @@ struct IndexScoreLaunch {
   float* scores; int64_t ld;
   CandArgs cand;    // cand.cand == nullptr: no candidate lists
   uint32_t* err;
+  int one_seq;      // 1: every token's key rows start at the same seq_kv
 };
+// Tokens per workgroup of the GEMM form of the indexer (one wave a token);
+// the workgroup reads the key rows of its first token for all of them.
+constexpr int kGemmTokens = 8;
+// Whether launch_index_score takes the GEMM form for these arguments.
+bool gemm_indexer(const IndexScoreLaunch& a);
 struct IndexPlan {
   int tiles_per_wave, wgs_per_token;
   int waves_per_token() const { return wgs_per_token * kIndexWaves; }
@@ -459,7 +465,16 @@ struct SelectLaunch {
   int lists_complete;  // 1: the lists are the whole candidate set, for rows of any length
   int32_t* idx; int32_t* count;
   uint32_t* err;
+  int row0_group;  // kGemmTokens after the GEMM indexer, else 0: see select_row0
 };
+// The key offset the select checks for token t.  After the GEMM indexer a
+// token whose seq_kv differs from that of the first token of its workgroup
+// was scored over no block (and raised BAD_META); -1 makes the select agree.
+__device__ __forceinline__ int64_t select_row0(const SelectLaunch& sl, int t) {
+  const int64_t r = sl.seq_kv[t];
+  if (sl.row0_group > 0 && sl.seq_kv[t - t % sl.row0_group] != r) return -1;
+  return r;
+}
 bool select_attend_fits(int T, int n_heads, int max_rows, int split_tiles);
 // 64-row tiles per split of the decode step's attention: kStepSplitTiles when
 // the select runs inside the attention kernel (small batches); otherwise as

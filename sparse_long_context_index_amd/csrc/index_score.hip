@@ -53,6 +53,22 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
 }
 
+// The same DMA, issued so that the compiler does not track it.  For a ring
+// of LDS tiles indexed at run time the compiler cannot tell which slot a
+// read touches and would wait for every DMA in flight before each read; the
+// ring's users order their reads with explicit vmcnt waits and barriers
+// instead.  (No VGPR is written: the data goes to LDS at M0 + 16 * lane.)
+__device__ __forceinline__ void lds_dma16_untracked(const void* gsrc, void* lds_dst) {
+  // M0 is kept as it was: the DMA reads it when it issues.
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(gsrc), "s"(m0)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt immediate");
@@ -69,6 +85,159 @@ __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcn
 // often.
 __device__ __forceinline__ int index_group(int L, int G) {
   return (G & 7) == 0 ? (L & ~7) | (((L & 7) + (L >> 3)) & 7) : L;
+}
+
+// Merges one scored tile into a wave's running candidate list while the next
+// tile's DMA is in flight: lanes r < m hold the r-th largest composite key of
+// the wave's blocks so far (sorted, descending; zero beyond its valid blocks)
+// and n_ok counts them.  Lanes 32..63 hold the tile's scores (part) for blocks
+// tile_blk0 + lane % 32 (the same scores as lanes 0..31); blocks at or past
+// n_vis are not keys.
+__device__ __forceinline__ void list_merge_tile(uint64_t& rl, uint32_t& n_ok, float part,
+                                                int64_t tile_blk0, int64_t n_vis, int m) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t b = tile_blk0 + col;
+  const bool tv = half == 1 && b < n_vis;
+  const uint32_t tsk = tv ? score_key(part) : 0u;
+  const uint64_t tkey = tsk != 0u ? ((uint64_t)tsk << 32) | (uint32_t)~(uint32_t)b : 0ull;
+  n_ok += (uint32_t)__popcll(__ballot(tv));
+  const uint64_t cut = readlane_u64(rl, m - 1);  // 0 until the list is full
+  uint64_t cmask = __ballot(tkey > cut);
+  const int nc = __popcll(cmask);
+  if (nc > 0 && nc <= 8) {
+    // few keys beat the list: insert each (lane i takes its own entry,
+    // the key, or the entry above it; m <= 32, so only lane 16 needs
+    // its upper neighbour from another row)
+    while (cmask != 0ull) {
+      const int l = __ffsll((unsigned long long)cmask) - 1;
+      cmask &= cmask - 1ull;
+      const uint64_t k = readlane_u64(tkey, l);
+      uint64_t prev = row_shr1_u64(rl);  // lane 0 of a row: all ones
+      const uint64_t r15 = readlane_u64(rl, 15);
+      if (lane == 16) prev = r15;
+      if (lane < m) rl = rl > k ? rl : (prev > k ? k : prev);
+    }
+  } else if (nc > 0 && m > kMergeRoundsMax) {
+    // Rank merge of the list (lanes 0..31, sorted, descending) with the
+    // tile (lanes 32..63): a key's rank is the number of larger keys
+    // among the 64 (keys are unique where nonzero).  A list key's rank
+    // is its lane plus the tile keys above it; a tile key's, the list
+    // keys and the tile keys above it.  Each key then moves to the
+    // lane of its rank (ds_permute), which keeps the list sorted.
+    const uint64_t mine = half == 1 ? tkey : rl;
+    uint32_t rank = half == 1 ? 0u : (uint32_t)lane;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const uint64_t tj = readlane_u64(tkey, 32 + j);
+      const uint64_t lj = readlane_u64(rl, j);
+      rank += tj > mine ? 1u : 0u;
+      if (half == 1) rank += lj > mine ? 1u : 0u;
+    }
+    const uint32_t nnz = (uint32_t)__popcll(__ballot(mine != 0ull));
+    const int addr = (int)(min(rank, 63u) * 4u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)(mine >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)mine);
+    const uint64_t got = ((uint64_t)hi << 32) | lo;
+    if (lane < m) rl = (uint32_t)lane < nnz ? got : 0ull;
+  } else if (nc > 0) {
+    // wave_m rounds over the list (lanes 0..31) and the tile (lanes
+    // 32..63): lane order is block order for equal scores
+    uint32_t sk = half == 1 ? tsk : (uint32_t)(rl >> 32);
+    const uint32_t lo = half == 1 ? (uint32_t)tkey : (uint32_t)rl;
+    const uint32_t avail = (uint32_t)__popcll(__ballot(sk != 0u));
+    const uint32_t take = avail < (uint32_t)m ? avail : (uint32_t)m;
+    uint64_t nrl = 0ull;
+    for (uint32_t r = 0; r < take; ++r) {
+      const uint64_t kr = wave_take_max(sk, lo);
+      if (lane == (int)r) nrl = kr;
+    }
+    rl = nrl;
+  }
+}
+
+// Exclusive prefix over the lanes of a per-lane count c < 8: three ballots
+// of its bits, each counted below the lane.
+__device__ __forceinline__ uint32_t lane_prefix8(uint32_t c, uint32_t* total) {
+  const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+  auto below = [](uint64_t b) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+  };
+  *total = (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+  return below(b0) + 2u * below(b1) + 4u * below(b2);
+}
+
+// One group's candidate list from its scores, all at once: the same list the
+// tile-by-tile merge above ends with (the m <= 32 largest composite keys of
+// the group's valid blocks), written to list[0 .. m) in block order with
+// zeros after the keys, and the group bound (the m-th key when more than m
+// blocks are valid, else zero) returned.  Lane l takes blocks blk0 + 4l + j,
+// j < 4, of the n_blk (a multiple of 32, at most 256) whose scores are
+// sc[0 .. n_blk); blocks at or past n_vis are not keys.  The m-th largest
+// score key is found bit by bit from the top (the largest x with at least m
+// keys >= x); keys above it are listed, and of the keys equal to it the
+// lowest blocks, as many as fill the list.
+__device__ __forceinline__ uint64_t group_list_from_scores(const float* sc, int n_blk,
+                                                           int64_t blk0, int64_t n_vis, int m,
+                                                           uint64_t* list) {
+  const int lane = threadIdx.x & 63;
+  const bool in = 4 * lane < n_blk;
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (in) v = *reinterpret_cast<const float4*>(sc + 4 * lane);
+  const float vs[4] = {v.x, v.y, v.z, v.w};
+  uint32_t sk[4];
+  uint32_t n_ok = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = in && blk0 + 4 * lane + j < n_vis;
+    sk[j] = ok ? score_key(vs[j]) : 0u;
+    n_ok += (uint32_t)__popcll(__ballot(ok));
+  }
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt += (uint32_t)__popcll(__ballot(sk[j] >= c));
+    if (cnt >= (uint32_t)m) thr = c;
+  }
+  // thr == 0: fewer than m nonzero keys, all listed
+  bool sel[4];
+  uint32_t n_gt = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) n_gt += (uint32_t)__popcll(__ballot(sk[j] > thr));
+  const uint32_t need = thr != 0u ? (uint32_t)m - n_gt : 0u;
+  uint32_t ce = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ce += (thr != 0u && sk[j] == thr) ? 1u : 0u;
+  uint32_t n_eq;
+  uint32_t r = lane_prefix8(ce, &n_eq);
+  uint32_t last_blk = 0;
+  bool has_last = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool eq = thr != 0u && sk[j] == thr;
+    sel[j] = sk[j] > thr || (eq && r < need);
+    if (eq && r + 1u == need) {
+      has_last = true;
+      last_blk = (uint32_t)(blk0 + 4 * lane + j);
+    }
+    r += eq ? 1u : 0u;
+  }
+  uint32_t cs = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cs += sel[j] ? 1u : 0u;
+  uint32_t n_sel;
+  uint32_t p = lane_prefix8(cs, &n_sel);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (sel[j]) list[p++] = ((uint64_t)sk[j] << 32) | (uint32_t)~(uint32_t)(blk0 + 4 * lane + j);
+  }
+  if (lane < m && (uint32_t)lane >= n_sel) list[lane] = 0ull;
+  const uint64_t hm = __ballot(has_last);
+  if (hm == 0ull || n_ok <= (uint32_t)m) return 0ull;
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)last_blk, __ffsll((unsigned long long)hm) - 1);
+  return ((uint64_t)thr << 32) | (uint32_t)~b;
 }
 
 // Up to 64 indexer heads the register budget is held to two waves per SIMD;
@@ -294,69 +463,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
       part += __shfl_xor(part, 32);
       if constexpr (F8) part *= ksc[j];
       sc[j] = part;
-      if (ca.cand != nullptr) {
-        // Merge this tile into the running list (sorted, descending) while
-        // the next tile's DMA is in flight.  Lanes 32..63 hold the tile's
-        // blocks (the same scores as lanes 0..31).
-        const int m = ca.wave_m;
-        const int64_t b = tile * kTileN + col;
-        const bool tv = half == 1 && b < n_vis;
-        const uint32_t tsk = tv ? score_key(part) : 0u;
-        const uint64_t tkey = tsk != 0u ? ((uint64_t)tsk << 32) | (uint32_t)~(uint32_t)b : 0ull;
-        n_ok += (uint32_t)__popcll(__ballot(tv));
-        const uint64_t cut = readlane_u64(rl, m - 1);  // 0 until the list is full
-        uint64_t cmask = __ballot(tkey > cut);
-        const int nc = __popcll(cmask);
-        if (nc > 0 && nc <= 8) {
-          // few keys beat the list: insert each (lane i takes its own entry,
-          // the key, or the entry above it; m <= 32, so only lane 16 needs
-          // its upper neighbour from another row)
-          while (cmask != 0ull) {
-            const int l = __ffsll((unsigned long long)cmask) - 1;
-            cmask &= cmask - 1ull;
-            const uint64_t k = readlane_u64(tkey, l);
-            uint64_t prev = row_shr1_u64(rl);  // lane 0 of a row: all ones
-            const uint64_t r15 = readlane_u64(rl, 15);
-            if (lane == 16) prev = r15;
-            if (lane < m) rl = rl > k ? rl : (prev > k ? k : prev);
-          }
-        } else if (nc > 0 && m > kMergeRoundsMax) {
-          // Rank merge of the list (lanes 0..31, sorted, descending) with the
-          // tile (lanes 32..63): a key's rank is the number of larger keys
-          // among the 64 (keys are unique where nonzero).  A list key's rank
-          // is its lane plus the tile keys above it; a tile key's, the list
-          // keys and the tile keys above it.  Each key then moves to the
-          // lane of its rank (ds_permute), which keeps the list sorted.
-          const uint64_t mine = half == 1 ? tkey : rl;
-          uint32_t rank = half == 1 ? 0u : (uint32_t)lane;
-#pragma unroll 8
-          for (int j = 0; j < 32; ++j) {
-            const uint64_t tj = readlane_u64(tkey, 32 + j);
-            const uint64_t lj = readlane_u64(rl, j);
-            rank += tj > mine ? 1u : 0u;
-            if (half == 1) rank += lj > mine ? 1u : 0u;
-          }
-          const uint32_t nnz = (uint32_t)__popcll(__ballot(mine != 0ull));
-          const int addr = (int)(min(rank, 63u) * 4u);
-          const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)(mine >> 32));
-          const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_permute(addr, (int)(uint32_t)mine);
-          const uint64_t got = ((uint64_t)hi << 32) | lo;
-          if (lane < m) rl = (uint32_t)lane < nnz ? got : 0ull;
-        } else if (nc > 0) {
-          // wave_m rounds over the list (lanes 0..31) and the tile (lanes
-          // 32..63): lane order is block order for equal scores
-          uint32_t sk = half == 1 ? tsk : (uint32_t)(rl >> 32);
-          const uint32_t lo = half == 1 ? (uint32_t)tkey : (uint32_t)rl;
-          const uint32_t avail = (uint32_t)__popcll(__ballot(sk != 0u));
-          const uint32_t take = avail < (uint32_t)m ? avail : (uint32_t)m;
-          uint64_t nrl = 0ull;
-          for (uint32_t r = 0; r < take; ++r) {
-            const uint64_t kr = wave_take_max(sk, lo);
-            if (lane == (int)r) nrl = kr;
-          }
-          rl = nrl;
-        }
-      }
+      if (ca.cand != nullptr) list_merge_tile(rl, n_ok, part, tile * kTileN, n_vis, ca.wave_m);
     }
   }
 
@@ -722,7 +829,212 @@ bool batch_indexer(int T, int n_ih, int ihd, int e4m3) {
   return T > 1 && T <= kBatchMaxT && n_ih <= 64 && !e4m3 && (ihd == 64 || ihd == 128);
 }
 
+// ---------------------------------------------------------------------------
+// Many query tokens of one sequence (a prefill chunk, one_seq): the scores of
+// T tokens are one GEMM of (tokens x heads) by blocks, and a key tile staged
+// once in LDS serves eight tokens.  A workgroup is eight waves, wave w scoring
+// token 8*blockIdx.y + w over kGemmGroups consecutive groups of the decode
+// plan (tiles_per_wave 32-block tiles each, so that the scores and candidate
+// lists come out exactly as the decode kernel's).  The eight waves share a
+// ring of kGemmSlots key tiles: wave p DMAs the p-th 1 KiB of every tile,
+// kGemmDepth tiles ahead, and one barrier per tile publishes a tile to all.
+// Queries and head weights stay in VGPRs.  Each wave keeps its token's
+// scores in LDS and stores them after the tile loop (a store among the
+// counted DMA waits would make the counts ambiguous: loads and stores share
+// the counter and need not complete in order); the candidate list of each
+// group is then built from the group's scores at once, not merged tile by
+// tile as in the decode kernel, which left the tile loop bound by that
+// merge's VALU work.
+constexpr int kGemmGroups = 4;
+constexpr int kGemmSlots = 12;
+constexpr int kGemmDepth = 8;
+constexpr int kGemmMinT = 64;
+static_assert(kGemmDepth < kGemmSlots, "a slot is refilled after every wave has used it");
+static_assert(kWaves == kGemmTokens, "one wave a token");
+
+template <int IHD, int MT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void index_gemm_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint16_t* __restrict__ k_idx, int64_t k_rows, const int64_t* __restrict__ pos,
+    const int64_t* __restrict__ seq_kv, const int32_t* __restrict__ n_comp, int T, int n_ih,
+    int ratio, float* __restrict__ scores, int64_t ld, CandArgs ca, uint32_t* __restrict__ err,
+    int tpw, int n_groups) {
+  constexpr int KS = IHD / 16;
+  constexpr int RB = 2 * IHD;             // bytes per key or query row
+  constexpr int CPR = RB / 16;            // 16-byte chunks per row
+  constexpr int TILE_CHUNKS = kTileN * CPR;
+  constexpr int LPT = TILE_CHUNKS / 64;   // DMA instructions (1 KiB) per tile: one per wave p < LPT
+  static_assert(LPT <= kWaves, "one DMA instruction per wave and tile");
+  constexpr int kMaxTiles = kGemmGroups * kMaxTpw;
+  __shared__ __attribute__((aligned(16))) u32x4 ring[kGemmSlots][TILE_CHUNKS];
+  __shared__ float s_sc[kWaves][kMaxTiles * kTileN];
+  __shared__ uint64_t s_list[kWaves][32];
+  __shared__ int64_t s_nvis[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int tw = blockIdx.y * kWaves + wave;   // this wave's token
+  const int t = tw < T ? tw : T - 1;
+  const int t0 = blockIdx.y * kWaves;          // its key rows serve the workgroup
+
+  // one round trip: the metadata, the queries (MFMA A operands: lane (col,
+  // half) holds head mt*32 + col, elements 16s + 8*half .. +8) and weights
+  const int64_t pos_t = pos[t];
+  const int32_t ncomp_t = n_comp[t];
+  const int64_t row0_t = seq_kv[t];
+  const int64_t row0 = seq_kv[t0];
+  u32x4 qa[MT][KS];
+  float wv[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int hq = mt * 32 + col < n_ih ? mt * 32 + col : n_ih - 1;
+    const uint16_t* qrow = q_idx + ((int64_t)t * n_ih + hq) * IHD;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qrow + (2 * s + half) * 8);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      wv[mt][r] = w[(int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1)];
+      if (hw >= n_ih) wv[mt][r] = 0.0f;
+    }
+  }
+  uint32_t flags = 0;
+  int64_t n_vis = visible_count(pos_t, ratio, ncomp_t, &flags);
+  if (row0_t < 0) {
+    flags |= CSA_DERR_BAD_META;
+    n_vis = 0;
+  } else if (row0_t + n_vis > k_rows) {
+    flags |= CSA_DERR_KEY_RANGE;
+    n_vis = 0;
+  }
+  if (n_vis > ld) {
+    flags |= CSA_DERR_VIS_OVER_LD;
+    n_vis = ld;
+  }
+  if (row0_t != row0 && n_vis > 0) {  // the promise of one sequence is broken
+    flags |= CSA_DERR_BAD_META;
+    n_vis = 0;
+  }
+  if (tw >= T) {
+    flags = 0;
+    n_vis = 0;
+  }
+  if (blockIdx.x == 0 && lane == 0) report(err, flags);
+  if (lane == 0) s_nvis[wave] = n_vis;
+  __syncthreads();
+  int64_t max_nvis = 0;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) max_nvis = max(max_nvis, s_nvis[v]);
+
+  // the workgroup's tiles: groups [gbeg, gend) of the row, up to the last
+  // tile that holds a visible block of one of its tokens
+  const int gbeg = blockIdx.x * kGemmGroups;
+  const int gend = min(gbeg + kGemmGroups, n_groups);
+  const int64_t tile0 = (int64_t)gbeg * tpw;
+  int nt = (gend - gbeg) * tpw;
+  const int64_t vis_tiles = (max_nvis + kTileN - 1) / kTileN - tile0;
+  if (vis_tiles < nt) nt = vis_tiles > 0 ? (int)vis_tiles : 0;
+  // every row read lies below max_nvis, the visible count of a token whose
+  // rows start at row0 and were checked against k_rows
+  const char* kbase = reinterpret_cast<const char*>(k_idx) + row0 * RB;
+  // tile i goes to ring slot i % kGemmSlots
+  auto issue = [&](int i) {
+    if (wave < LPT) {  // instruction `wave` of tile i: rows (64*wave + lane) / CPR
+      const int e = wave * 64 + lane;
+      const int r = e / CPR, p = e % CPR;
+      const int c = p ^ (r & (CPR - 1));
+      int64_t blk = (tile0 + i) * kTileN + r;
+      if (blk > max_nvis - 1) blk = max_nvis - 1;
+      lds_dma16_untracked(kbase + blk * RB + c * 16, &ring[i % kGemmSlots][wave * 64]);
+    }
+  };
+  for (int i = 0; i < kGemmDepth && i < nt; ++i) issue(i);
+
+  for (int i = 0; i < nt; ++i) {
+    // this wave's part of tile i has landed (one DMA per tile and wave, no
+    // other memory operation in flight), then every wave's part has
+    if (i + kGemmDepth - 1 < nt) wait_vmcnt<kGemmDepth - 1>(); else wait_vmcnt<0>();
+    __syncthreads();  // tile i is complete; every wave is done with tile i - 1
+    // the next DMA goes into the slot that tile i + depth - slots left
+    if (i + kGemmDepth < nt) issue(i + kGemmDepth);
+    const int64_t tt = tile0 + i;
+    if (tt * kTileN < n_vis) {  // wave-uniform: the token sees a block of the tile
+      const u32x4* kt = ring[i % kGemmSlots];
+      u32x4 kb[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kb[s] = kt[col * CPR + ((2 * s + half) ^ (col & (CPR - 1)))];
+      f32x16 acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[mt][s]),
+                                                            __builtin_bit_cast(bf16x8, kb[s]), acc[mt],
+                                                            0, 0, 0);
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+      }
+      part += __shfl_xor(part, 32);
+      if (half == 0) s_sc[wave][i * kTileN + col] = part;
+    }
+  }
+
+  // after the loop (its last wait drained every DMA): this wave's scores,
+  // two tiles per store, and one list per group (empty past the tiles)
+  if (tw >= T) return;
+  float* srow = scores + (int64_t)tw * ld;
+  for (int i = half; i < nt; i += 2) {
+    const int64_t blk = (tile0 + i) * kTileN + col;
+    if (blk < n_vis) srow[blk] = s_sc[wave][i * kTileN + col];
+  }
+  if (ca.cand != nullptr) {
+    // one list per group (empty past the tiles), in block order
+    uint64_t* lst = s_list[wave];
+    for (int gi = 0; gi < gend - gbeg; ++gi) {
+      const int64_t g = (int64_t)tw * ca.groups_per_token + gbeg + gi;
+      const int64_t gb0 = (tile0 + (int64_t)gi * tpw) * kTileN;
+      const uint64_t bound = gi * tpw < nt
+          ? group_list_from_scores(&s_sc[wave][gi * tpw * kTileN], tpw * kTileN, gb0, n_vis,
+                                   ca.wave_m, lst)
+          : 0ull;
+      if (gi * tpw >= nt && lane < ca.wave_m) lst[lane] = 0ull;
+      if (lane < ca.wave_m) ca.cand[g * ca.list_len + lane] = lst[lane];
+      if (lane == 0) ca.gcut[g] = bound;
+    }
+  }
+}
+
+template <int IHD>
+hipError_t launch_gemm_ihd(const IndexScoreLaunch& a, const IndexPlan& p, hipStream_t s) {
+  const int n_groups = p.waves_per_token();
+  const dim3 grid((unsigned)((n_groups + kGemmGroups - 1) / kGemmGroups),
+                  (unsigned)((a.T + kWaves - 1) / kWaves));
+  const auto* q = static_cast<const uint16_t*>(a.q_idx);
+  const auto* k = static_cast<const uint16_t*>(a.k_idx);
+  if (a.n_ih <= 32)
+    hipLaunchKernelGGL((index_gemm_kernel<IHD, 1>), grid, dim3(kWaves * 64), 0, s, q, a.w, k,
+                       a.k_rows, a.pos, a.seq_kv, a.n_comp, a.T, a.n_ih, a.ratio, a.scores, a.ld,
+                       a.cand, a.err, p.tiles_per_wave, n_groups);
+  else
+    hipLaunchKernelGGL((index_gemm_kernel<IHD, 2>), grid, dim3(kWaves * 64), 0, s, q, a.w, k,
+                       a.k_rows, a.pos, a.seq_kv, a.n_comp, a.T, a.n_ih, a.ratio, a.scores, a.ld,
+                       a.cand, a.err, p.tiles_per_wave, n_groups);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool gemm_indexer(const IndexScoreLaunch& a) {
+  return a.one_seq && !a.e4m3 && a.T >= kGemmMinT && a.n_ih <= 64 && (a.ihd == 64 || a.ihd == 128) &&
+         (a.cand.cand == nullptr || !a.cand.merge);
+}
 
 IndexPlan plan_index(int T, int64_t ld) {
   // Every wave owns `tpw` consecutive 32-block tiles; about one resident
@@ -754,6 +1066,7 @@ hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s) {
     return a.ihd == 64 ? launch_batch_ihd<64>(a, s) : launch_batch_ihd<128>(a, s);
   }
   const IndexPlan& p = bp;
+  if (gemm_indexer(a)) return a.ihd == 64 ? launch_gemm_ihd<64>(a, p, s) : launch_gemm_ihd<128>(a, p, s);
   switch (a.ihd) {
     case 32: return launch_ihd<32>(a, p, s);
     case 64: return launch_ihd<64>(a, p, s);

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(sel::kThreads) void step_select_kernel(SelectLaunch
   const int t = blockIdx.x;
   int32_t* out = sl.idx + (int64_t)t * sl.top_k;
   const sel::SelResult r = sel::step_select<sel::kThreads, KP>(
-      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, sl.seq_kv[t],
+      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, select_row0(sl, t),
       sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
       sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
       sl.blocks_per_group, sl.lists_complete != 0, u.f, u.s, out, 0u, (uint32_t)sl.top_k);

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert b.csa_abi_version() == 2
+    assert b.csa_abi_version() == 3
     assert b.csa_status_str(0) == "CSA_OK"
     for s in (1, 2, 3, 4):
         assert b.csa_status_str(s).startswith("CSA_E")
@@ -168,6 +168,12 @@ def test_decode_step_validation(lib):
     assert st(FAKE, need) == b.CSA_EWORKSPACE
     a.k_idx8 = FAKE + 8           # codes are read 16 bytes at a time
     assert st(FAKE, need8) == b.CSA_EINVAL
+    a.idx_e4m3 = 0
+    a.k_idx8 = FAKE
+    a.one_sequence = 2            # a flag: 0 or 1
+    assert st(FAKE, need) == b.CSA_EINVAL
+    a.one_sequence = 1            # no workspace of its own
+    assert b.csa_decode_step_workspace_bytes(a) == need
     a.k_idx8 = FAKE
     a.idx_e4m3 = 2
     assert st(FAKE, need8) == b.CSA_EINVAL
