@@ -26,6 +26,13 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ReLU on the bits: a float with the sign bit set (negative, -0, -inf, a
+// NaN with the sign set) becomes +0, any other keeps its value.  One integer
+// max, where fmaxf(x, 0) would first canonicalize x (a second instruction).
+__device__ __forceinline__ float relu_f32(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Composite selection key of block s with score f: the score key in the high
 // word, the complemented block index in the low word.  Unique per block;
 // larger score first, then lower block index.  Zero marks an empty slot.

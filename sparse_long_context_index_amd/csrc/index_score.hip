@@ -167,77 +167,127 @@ __device__ __forceinline__ uint32_t lane_prefix8(uint32_t c, uint32_t* total) {
   return below(b0) + 2u * below(b1) + 4u * below(b2);
 }
 
-// One group's candidate list from its scores, all at once: the same list the
-// tile-by-tile merge above ends with (the m <= 32 largest composite keys of
-// the group's valid blocks), written to list[0 .. m) in block order with
-// zeros after the keys, and the group bound (the m-th key when more than m
-// blocks are valid, else zero) returned.  Lane l takes blocks blk0 + 4l + j,
-// j < 4, of the n_blk (a multiple of 32, at most 256) whose scores are
-// sc[0 .. n_blk); blocks at or past n_vis are not keys.  The m-th largest
-// score key is found bit by bit from the top (the largest x with at least m
-// keys >= x); keys above it are listed, and of the keys equal to it the
-// lowest blocks, as many as fill the list.
-__device__ __forceinline__ uint64_t group_list_from_scores(const float* sc, int n_blk,
-                                                           int64_t blk0, int64_t n_vis, int m,
-                                                           uint64_t* list) {
+// The candidate lists of NG consecutive groups of one token from their
+// scores, all at once.  Each group gets the list the tile-by-tile merge above
+// ends with (the m <= 32 largest composite keys of its valid blocks), stored
+// in block order with zeros after the keys, and its bound (the m-th key when
+// more than m blocks are valid, else zero).  Group g's n_blk blocks (a
+// multiple of 32, at most 256) start at block blk0 + g * n_blk, their scores
+// at sc + g * n_blk, and lane l takes blocks 4l + j, j < 4; groups g >= n_live
+// hold no tiles (empty lists), groups g >= n_store are not stored, and blocks
+// at or past n_vis are not keys.  A group's m-th largest score key is found
+// bit by bit from the top (the largest x with at least m keys >= x), the
+// groups' searches in lockstep so that their ballot and count chains overlap;
+// a group stops as soon as exactly m keys lie at or above its prefix.
+template <int NG>
+__device__ __forceinline__ void groups_lists_from_scores(const float* sc, int n_blk, int64_t blk0,
+                                                         int64_t n_vis, int m, int n_live,
+                                                         int n_store, uint64_t* cand, int list_len,
+                                                         uint64_t* gcut) {
   const int lane = threadIdx.x & 63;
   const bool in = 4 * lane < n_blk;
-  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (in) v = *reinterpret_cast<const float4*>(sc + 4 * lane);
-  const float vs[4] = {v.x, v.y, v.z, v.w};
-  uint32_t sk[4];
-  uint32_t n_ok = 0;
+  uint32_t sk[NG][4];
+  uint32_t n_ok[NG];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool ok = in && blk0 + 4 * lane + j < n_vis;
-    sk[j] = ok ? score_key(vs[j]) : 0u;
-    n_ok += (uint32_t)__popcll(__ballot(ok));
-  }
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = thr | (1u << bit);
-    uint32_t cnt = 0;
+  for (int g = 0; g < NG; ++g) {
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (in && g < n_live) v = *reinterpret_cast<const float4*>(sc + g * n_blk + 4 * lane);
+    const float vs[4] = {v.x, v.y, v.z, v.w};
+    n_ok[g] = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cnt += (uint32_t)__popcll(__ballot(sk[j] >= c));
-    if (cnt >= (uint32_t)m) thr = c;
-  }
-  // thr == 0: fewer than m nonzero keys, all listed
-  bool sel[4];
-  uint32_t n_gt = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) n_gt += (uint32_t)__popcll(__ballot(sk[j] > thr));
-  const uint32_t need = thr != 0u ? (uint32_t)m - n_gt : 0u;
-  uint32_t ce = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ce += (thr != 0u && sk[j] == thr) ? 1u : 0u;
-  uint32_t n_eq;
-  uint32_t r = lane_prefix8(ce, &n_eq);
-  uint32_t last_blk = 0;
-  bool has_last = false;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const bool eq = thr != 0u && sk[j] == thr;
-    sel[j] = sk[j] > thr || (eq && r < need);
-    if (eq && r + 1u == need) {
-      has_last = true;
-      last_blk = (uint32_t)(blk0 + 4 * lane + j);
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = in && g < n_live && blk0 + (int64_t)g * n_blk + 4 * lane + j < n_vis;
+      sk[g][j] = ok ? score_key(vs[j]) : 0u;
+      n_ok[g] += (uint32_t)__popcll(__ballot(ok));
     }
-    r += eq ? 1u : 0u;
   }
-  uint32_t cs = 0;
+  // thr[g]: the largest value found so far with at least m keys >= it, and
+  // cnt[g] how many keys are >= it.  A group is done once exactly m keys are
+  // >= thr (then they are its list, whatever the lower bits of the m-th); the
+  // search stops when every group is done or the last bit is decided.
+  // A group of fewer than m nonzero keys is done at once (thr = 0).
+  uint32_t thr[NG], cnt[NG];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cs += sel[j] ? 1u : 0u;
-  uint32_t n_sel;
-  uint32_t p = lane_prefix8(cs, &n_sel);
+  for (int g = 0; g < NG; ++g) {
+    uint32_t nz = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (sel[j]) list[p++] = ((uint64_t)sk[j] << 32) | (uint32_t)~(uint32_t)(blk0 + 4 * lane + j);
+    for (int j = 0; j < 4; ++j) nz += (uint32_t)__popcll(__ballot(sk[g][j] != 0u));
+    thr[g] = 0u;
+    cnt[g] = nz < (uint32_t)m ? (uint32_t)m : 256u;  // every slot is >= 0
   }
-  if (lane < m && (uint32_t)lane >= n_sel) list[lane] = 0ull;
-  const uint64_t hm = __ballot(has_last);
-  if (hm == 0ull || n_ok <= (uint32_t)m) return 0ull;
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)last_blk, __ffsll((unsigned long long)hm) - 1);
-  return ((uint64_t)thr << 32) | (uint32_t)~b;
+  for (int bit = 31; bit >= 0; --bit) {
+    bool all_done = true;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (cnt[g] == (uint32_t)m) continue;
+      all_done = false;
+      const uint32_t c = thr[g] | (1u << bit);
+      uint32_t n = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) n += (uint32_t)__popcll(__ballot(sk[g][j] >= c));
+      if (n >= (uint32_t)m) {
+        thr[g] = c;
+        cnt[g] = n;
+      }
+    }
+    if (all_done) break;
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g >= n_store) break;
+    uint64_t* list = cand + (int64_t)g * list_len;
+    const int64_t gb0 = blk0 + (int64_t)g * n_blk;
+    // thr == 0: fewer than m nonzero keys, all listed.  cnt == m: the m keys
+    // >= thr (thr > 0).  Otherwise thr is the m-th largest score key itself, shared by
+    // several blocks: the keys above it, and of those equal to it the lowest
+    // blocks, as many as fill the list.
+    uint32_t need = 0;
+    if (thr[g] != 0u && cnt[g] != (uint32_t)m) {
+      uint32_t n_gt = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) n_gt += (uint32_t)__popcll(__ballot(sk[g][j] > thr[g]));
+      need = (uint32_t)m - n_gt;
+    }
+    bool sel[4];
+    uint32_t ce = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ce += (need != 0u && sk[g][j] == thr[g]) ? 1u : 0u;
+    uint32_t n_eq;
+    uint32_t r = lane_prefix8(ce, &n_eq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool eq = need != 0u && sk[g][j] == thr[g];
+      sel[j] = thr[g] == 0u ? sk[g][j] != 0u
+                            : (need == 0u ? sk[g][j] >= thr[g] : (sk[g][j] > thr[g] || (eq && r < need)));
+      r += eq ? 1u : 0u;
+    }
+    uint32_t cs = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cs += sel[j] ? 1u : 0u;
+    uint32_t n_sel;
+    uint32_t p = lane_prefix8(cs, &n_sel);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (sel[j]) list[p++] = ((uint64_t)sk[g][j] << 32) | (uint32_t)~(uint32_t)(gb0 + 4 * lane + j);
+    }
+    if (lane < m && (uint32_t)lane >= n_sel) list[lane] = 0ull;
+    // the bound: the smallest listed composite key (the smallest listed
+    // score key, at the highest block that holds it), when blocks were left out
+    uint64_t bound = 0ull;
+    if (n_ok[g] > (uint32_t)m && thr[g] != 0u) {
+      uint32_t lo = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lo = max(lo, sel[j] ? ~sk[g][j] : 0u);
+      const uint32_t smin = ~wave_max_u32(lo);
+      uint32_t hb = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hb = max(hb, sel[j] && sk[g][j] == smin ? (uint32_t)(gb0 + 4 * lane + j) + 1u : 0u);
+      const uint32_t b = wave_max_u32(hb) - 1u;
+      bound = ((uint64_t)smin << 32) | (uint32_t)~b;
+    }
+    if (lane == 0) gcut[g] = bound;
+  }
 }
 
 // Up to 64 indexer heads the register budget is held to two waves per SIMD;
@@ -458,7 +508,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(MT 
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+        for (int r = 0; r < 16; ++r) part += wv[mt][r] * relu_f32(acc[mt][r]);
       }
       part += __shfl_xor(part, 32);
       if constexpr (F8) part *= ksc[j];
@@ -666,7 +716,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+      for (int r = 0; r < 16; ++r) part += wv[mt][r] * relu_f32(acc[mt][r]);
     }
     part += __shfl_xor(part, 32);
 
@@ -789,7 +839,7 @@ __global__ __launch_bounds__(256) void rescore_kernel(RescoreLaunch a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+    for (int r = 0; r < 16; ++r) part += wv[mt][r] * relu_f32(acc[mt][r]);
   }
   part += __shfl_xor(part, 32);
   const uint32_t sk = score_key(part);
@@ -868,7 +918,6 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int kMaxTiles = kGemmGroups * kMaxTpw;
   __shared__ __attribute__((aligned(16))) u32x4 ring[kGemmSlots][TILE_CHUNKS];
   __shared__ float s_sc[kWaves][kMaxTiles * kTileN];
-  __shared__ uint64_t s_list[kWaves][32];
   __shared__ int64_t s_nvis[kWaves];
 
   const int lane = threadIdx.x & 63;
@@ -951,38 +1000,62 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   };
   for (int i = 0; i < kGemmDepth && i < nt; ++i) issue(i);
 
-  for (int i = 0; i < nt; ++i) {
-    // this wave's part of tile i has landed (one DMA per tile and wave, no
-    // other memory operation in flight), then every wave's part has
-    if (i + kGemmDepth - 1 < nt) wait_vmcnt<kGemmDepth - 1>(); else wait_vmcnt<0>();
-    __syncthreads();  // tile i is complete; every wave is done with tile i - 1
-    // the next DMA goes into the slot that tile i + depth - slots left
+  // two tiles a step: one barrier per pair, and two independent MFMA chains
+  // per wave (the epilogue of one overlaps the products of the other)
+  for (int i = 0; i < nt; i += 2) {
+    const bool two = i + 1 < nt;
+    // this wave's parts of tiles i and i + 1 have landed (one DMA per tile
+    // and wave, no other memory operation in flight), then every wave's have
+    if (i + kGemmDepth <= nt) wait_vmcnt<kGemmDepth - 2>(); else wait_vmcnt<0>();
+    __syncthreads();  // tiles i, i + 1 complete; every wave is done with i - 2, i - 1
+    // the next DMAs go into the slots that tiles i + depth - slots, + 1 left
     if (i + kGemmDepth < nt) issue(i + kGemmDepth);
+    if (i + kGemmDepth + 1 < nt) issue(i + kGemmDepth + 1);
     const int64_t tt = tile0 + i;
-    if (tt * kTileN < n_vis) {  // wave-uniform: the token sees a block of the tile
-      const u32x4* kt = ring[i % kGemmSlots];
-      u32x4 kb[KS];
+    if (tt * kTileN < n_vis) {  // wave-uniform: the token sees a block of tile i
+      // a lone last tile is computed twice and kept once
+      const u32x4* kt0 = ring[i % kGemmSlots];
+      const u32x4* kt1 = ring[(two ? i + 1 : i) % kGemmSlots];
+      u32x4 kb0[KS], kb1[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kb[s] = kt[col * CPR + ((2 * s + half) ^ (col & (CPR - 1)))];
-      f32x16 acc[MT];
+      for (int s = 0; s < KS; ++s) {
+        const int c = col * CPR + ((2 * s + half) ^ (col & (CPR - 1)));
+        kb0[s] = kt0[c];
+        kb1[s] = kt1[c];
+      }
+      f32x16 acc0[MT], acc1[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+      for (int mt = 0; mt < MT; ++mt) {
+        acc0[mt] = f32x16{};
+        acc1[mt] = f32x16{};
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[mt][s]),
-                                                            __builtin_bit_cast(bf16x8, kb[s]), acc[mt],
-                                                            0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) {
+          acc0[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[mt][s]),
+                                                             __builtin_bit_cast(bf16x8, kb0[s]), acc0[mt],
+                                                             0, 0, 0);
+          acc1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[mt][s]),
+                                                             __builtin_bit_cast(bf16x8, kb1[s]), acc1[mt],
+                                                             0, 0, 0);
+        }
       }
-      float part = 0.0f;
+      float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part += wv[mt][r] * fmaxf(acc[mt][r], 0.0f);
+        for (int r = 0; r < 16; ++r) {
+          part0 += wv[mt][r] * relu_f32(acc0[mt][r]);
+          part1 += wv[mt][r] * relu_f32(acc1[mt][r]);
+        }
       }
-      part += __shfl_xor(part, 32);
-      if (half == 0) s_sc[wave][i * kTileN + col] = part;
+      part0 += __shfl_xor(part0, 32);
+      part1 += __shfl_xor(part1, 32);
+      if (half == 0) {
+        s_sc[wave][i * kTileN + col] = part0;
+        if (two) s_sc[wave][(i + 1) * kTileN + col] = part1;
+      }
     }
   }
 
@@ -996,18 +1069,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
   if (ca.cand != nullptr) {
     // one list per group (empty past the tiles), in block order
-    uint64_t* lst = s_list[wave];
-    for (int gi = 0; gi < gend - gbeg; ++gi) {
-      const int64_t g = (int64_t)tw * ca.groups_per_token + gbeg + gi;
-      const int64_t gb0 = (tile0 + (int64_t)gi * tpw) * kTileN;
-      const uint64_t bound = gi * tpw < nt
-          ? group_list_from_scores(&s_sc[wave][gi * tpw * kTileN], tpw * kTileN, gb0, n_vis,
-                                   ca.wave_m, lst)
-          : 0ull;
-      if (gi * tpw >= nt && lane < ca.wave_m) lst[lane] = 0ull;
-      if (lane < ca.wave_m) ca.cand[g * ca.list_len + lane] = lst[lane];
-      if (lane == 0) ca.gcut[g] = bound;
-    }
+    const int64_t g0 = (int64_t)tw * ca.groups_per_token + gbeg;
+    groups_lists_from_scores<kGemmGroups>(s_sc[wave], tpw * kTileN, tile0 * kTileN, n_vis,
+                                          ca.wave_m, (nt + tpw - 1) / tpw, gend - gbeg,
+                                          ca.cand + g0 * ca.list_len, ca.list_len, ca.gcut + g0);
   }
 }
 
