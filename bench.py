@@ -185,6 +185,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-configs", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated names of the other workloads to run (e4m3_1m, ctx_32k, "
+                         "batched_32, prefill_4096, producer, hca_1m); all by default")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -306,7 +309,8 @@ def main() -> int:
 
     configs = {}
     if not args.no_configs:
-        configs = other_configs(torch, B, gen, R, dev, stream, layered, check_err, log)
+        configs = other_configs(torch, B, gen, R, dev, stream, layered, check_err, log,
+                                only=None if args.only is None else set(args.only.split(",")))
     del layers, sargs, ws
     torch.cuda.empty_cache()
 
@@ -351,10 +355,14 @@ def main() -> int:
     return 0
 
 
-def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dict:
-    """The other workloads, each as graph replays of rotated layers."""
+def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log, only=None) -> dict:
+    """The other workloads, each as graph replays of rotated layers (only: the
+    names of those to run, all when None)."""
     import numpy as np
     res = {}
+
+    def want(name):
+        return only is None or name in only
 
     def csa_config(name, inp, n_layers, replays, e4m3=False, index_stage=False, one_sequence=False):
         layers = layered(inp, n_layers, e4m3=e4m3)
@@ -374,142 +382,148 @@ def other_configs(torch, B, gen, R, dev, stream, layered, check_err, log) -> dic
         torch.cuda.empty_cache()
         return r
 
-    # E4M3 indexer keys at 1M
-    log("config: 1M step with E4M3 indexer keys")
-    inp = gen.ctx1m()
-    r = csa_config("e4m3_1m", inp, LAYERS, 20, e4m3=True, index_stage=True)
-    ib = index_bytes(inp, lists_words(1, inp.max_visible()), e4m3=True)
-    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
-    r["index_gbs"] = round(ib / (r["index_us"]["median"] * 1e-6) / 1e9, 1)
-    r["index_frac"] = round(r["index_gbs"] / HBM_PEAK_GBS, 4)
-    r["index_bytes"] = ib
-    r["workload"] = ("1M-context CSA decode step with E4M3 indexer keys and queries "
-                     "(prefilter of 1536, bf16 rescore)")
-    res["e4m3_1m"] = r
+    if want("e4m3_1m"):
+        # E4M3 indexer keys at 1M
+        log("config: 1M step with E4M3 indexer keys")
+        inp = gen.ctx1m()
+        r = csa_config("e4m3_1m", inp, LAYERS, 20, e4m3=True, index_stage=True)
+        ib = index_bytes(inp, lists_words(1, inp.max_visible()), e4m3=True)
+        r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+        r["index_gbs"] = round(ib / (r["index_us"]["median"] * 1e-6) / 1e9, 1)
+        r["index_frac"] = round(r["index_gbs"] / HBM_PEAK_GBS, 4)
+        r["index_bytes"] = ib
+        r["workload"] = ("1M-context CSA decode step with E4M3 indexer keys and queries "
+                         "(prefilter of 1536, bf16 rescore)")
+        res["e4m3_1m"] = r
 
-    # 32K context
-    log("config: 32K-context step")
-    inp = gen.ctx32k()
-    r = csa_config("ctx_32k", inp, LAYERS, 20)
-    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
-    r["workload"] = "32K-context CSA decode step: 8192 blocks, batch 1"
-    res["ctx_32k"] = r
+    if want("ctx_32k"):
+        # 32K context
+        log("config: 32K-context step")
+        inp = gen.ctx32k()
+        r = csa_config("ctx_32k", inp, LAYERS, 20)
+        r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+        r["workload"] = "32K-context CSA decode step: 8192 blocks, batch 1"
+        res["ctx_32k"] = r
 
-    # batch of 32 sequences
-    log("config: batch of 32 sequences")
-    inp = gen.batched()
-    r = csa_config("batched_32", inp, 4, 20)
-    sb = step_bytes(inp)
-    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
-    r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
-    r["min_bytes"] = sb
-    r["gbs"] = round(sb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
-    r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
-    r["workload"] = "32 sequences, lengths uniform in [16K, 128K], one decode token each"
-    res["batched_32"] = r
+    if want("batched_32"):
+        # batch of 32 sequences
+        log("config: batch of 32 sequences")
+        inp = gen.batched()
+        r = csa_config("batched_32", inp, 4, 20)
+        sb = step_bytes(inp)
+        r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+        r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
+        r["min_bytes"] = sb
+        r["gbs"] = round(sb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
+        r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+        r["workload"] = "32 sequences, lengths uniform in [16K, 128K], one decode token each"
+        res["batched_32"] = r
 
-    # 4096-token prefill chunk
-    log("config: 4096-token prefill chunk")
-    inp = gen.prefill()
-    # one sequence: the indexer runs as one GEMM whose key tiles serve eight tokens
-    r = csa_config("prefill_4096", inp, 1, 5, index_stage=True, one_sequence=True)
-    flops = 0
-    for t in range(inp.T):
-        n = min(int(inp.pos[t]) // inp.ratio, int(inp.n_comp[t]))
-        flops += 2 * n * inp.n_ih * inp.ihd
-    r["index_tflops"] = round(flops / (r["index_us"]["median"] * 1e-6) / 1e12, 1)
-    r["index_frac_bf16_mfma"] = round(r["index_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
-    r["index_flops"] = flops
-    r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
-    r["workload"] = "prefill chunk: 4096 query tokens at positions 61440..65535, 16384 blocks"
-    res["prefill_4096"] = r
+    if want("prefill_4096"):
+        # 4096-token prefill chunk
+        log("config: 4096-token prefill chunk")
+        inp = gen.prefill()
+        # one sequence: the indexer runs as one GEMM whose key tiles serve eight tokens
+        r = csa_config("prefill_4096", inp, 1, 5, index_stage=True, one_sequence=True)
+        flops = 0
+        for t in range(inp.T):
+            n = min(int(inp.pos[t]) // inp.ratio, int(inp.n_comp[t]))
+            flops += 2 * n * inp.n_ih * inp.ihd
+        r["index_tflops"] = round(flops / (r["index_us"]["median"] * 1e-6) / 1e12, 1)
+        r["index_frac_bf16_mfma"] = round(r["index_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)
+        r["index_flops"] = flops
+        r["tokens_per_s"] = round(inp.T * 1e6 / r["step_us"]["median"], 1)
+        r["workload"] = "prefill chunk: 4096 query tokens at positions 61440..65535, 16384 blocks"
+        res["prefill_4096"] = r
 
-    # producer side: the compressors and cache append of one decode step
-    for T in (1, 32):
-        log(f"config: producer step, {T} token(s)")
-        pinp = gen.producer_1m(T=T)
-        nl = LAYERS
-        bfp = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
-        i64 = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)  # noqa: E731
-        x = bfp(pinp.x)
-        wk0, wi0 = bfp(pinp.w_kv), bfp(pinp.w_ik)
-        wks = [wk0] + [wk0.clone() for _ in range(nl - 1)]
-        wis = [wi0] + [wi0.clone() for _ in range(nl - 1)]
-        st = dict(seq=i64(pinp.seq, np.int32), pos=i64(pinp.pos, np.int64),
-                  ring=i64(pinp.ring, np.float32), swa=bfp(pinp.swa),
-                  swa_head=i64(pinp.swa_head, np.int32), swa_len=i64(pinp.swa_len, np.int32),
-                  comp_kv=bfp(pinp.comp_kv), k_idx=bfp(pinp.k_idx),
-                  seq_kv=i64(pinp.seq_kv, np.int64), n_comp=i64(pinp.n_comp, np.int32))
-        pws = torch.empty(B.csa_compress_append_workspace_bytes(T, pinp.H, pinp.hd, pinp.ihd),
-                          dtype=torch.uint8, device=dev)
-        perr = torch.zeros(1, dtype=torch.int32, device=dev)
+    if want("producer"):
+        # producer side: the compressors and cache append of one decode step
+        for T in (1, 32):
+            log(f"config: producer step, {T} token(s)")
+            pinp = gen.producer_1m(T=T)
+            nl = LAYERS
+            bfp = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+            i64 = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)  # noqa: E731
+            x = bfp(pinp.x)
+            wk0, wi0 = bfp(pinp.w_kv), bfp(pinp.w_ik)
+            wks = [wk0] + [wk0.clone() for _ in range(nl - 1)]
+            wis = [wi0] + [wi0.clone() for _ in range(nl - 1)]
+            st = dict(seq=i64(pinp.seq, np.int32), pos=i64(pinp.pos, np.int64),
+                      ring=i64(pinp.ring, np.float32), swa=bfp(pinp.swa),
+                      swa_head=i64(pinp.swa_head, np.int32), swa_len=i64(pinp.swa_len, np.int32),
+                      comp_kv=bfp(pinp.comp_kv), k_idx=bfp(pinp.k_idx),
+                      seq_kv=i64(pinp.seq_kv, np.int64), n_comp=i64(pinp.n_comp, np.int32))
+            pws = torch.empty(B.csa_compress_append_workspace_bytes(T, pinp.H, pinp.hd, pinp.ihd),
+                              dtype=torch.uint8, device=dev)
+            perr = torch.zeros(1, dtype=torch.int32, device=dev)
 
-        def pcall(i):
-            return lambda: B.csa_compress_append(
-                x, wks[i], wis[i], st["seq"], st["pos"], pinp.ratio, pinp.window, st["ring"],
-                st["swa"], st["swa_head"], st["swa_len"], st["comp_kv"], st["k_idx"],
-                st["seq_kv"], st["n_comp"], pws, err=perr)
-        g = R.capture([pcall(i) for i in range(nl)])
+            def pcall(i):
+                return lambda: B.csa_compress_append(
+                    x, wks[i], wis[i], st["seq"], st["pos"], pinp.ratio, pinp.window, st["ring"],
+                    st["swa"], st["swa_head"], st["swa_len"], st["comp_kv"], st["k_idx"],
+                    st["seq_kv"], st["n_comp"], pws, err=perr)
+            g = R.capture([pcall(i) for i in range(nl)])
+            ms = R.replays(g, nl, 20)
+            torch.cuda.synchronize()
+            # the same positions are replayed: the appends repeat the same rows
+            # and may flag the n_comp bookkeeping; only range errors count here
+            if int(perr.item()) & ~0x4:
+                raise RuntimeError(f"producer: device error word {int(perr.item()):#x}")
+            wbytes = (2 * pinp.hd + 2 * pinp.ihd) * pinp.H * 2
+            pb = wbytes + T * (pinp.H * 2 + (2 * pinp.hd + 2 * pinp.ihd) * 4 + pinp.hd * 2)
+            r = {"step_us": _dist_us(ms), "min_bytes": pb}
+            r["gbs"] = round(pb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
+            r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
+            r["workload"] = (f"producer of one decode step, {T} token(s): both compressors' "
+                             "projections (H 7168 -> 2x512 + 2x128), ring, window append, pooling")
+            res[f"producer_{T}"] = r
+            del wks, wis, g, st, pws
+            torch.cuda.empty_cache()
+
+    if want("hca_1m"):
+        # dense HCA at 1M
+        log("config: dense HCA step at 1M")
+        h = gen.hca1m()
+        nl = 60  # 60 x 8.5 MB of rows: well past the last-level cache
+
+        def tdev(a, dt):
+            return torch.as_tensor(a).to(dev) if dt is None else torch.as_tensor(a, dtype=dt).to(dev)
+
+        bf = lambda a: torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)  # noqa: E731
+        base = {"q": bf(h.q), "swa": bf(h.swa), "pos": tdev(h.pos, torch.int64),
+                "seq_kv": tdev(h.seq_kv, torch.int64), "n_comp": tdev(h.n_comp, torch.int32),
+                "swa_row0": tdev(h.swa_row0, torch.int64), "swa_len": tdev(h.swa_len, torch.int32)}
+        kv0 = bf(h.comp_kv)
+        kvs = [kv0] + [kv0.clone() for _ in range(nl - 1)]
+        out = torch.zeros((h.T, h.n_heads, h.head_dim), dtype=torch.bfloat16, device=dev)
+        lse = torch.zeros((h.T, h.n_heads), dtype=torch.float32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        hargs = []
+        for kv in kvs:
+            a = B.StepArgs()
+            a.mode, a.T, a.ratio, a.window = B.CSA_MODE_HCA, h.T, h.ratio, 128
+            a.n_heads, a.head_dim, a.max_vis, a.scale = h.n_heads, h.head_dim, 8192, h.scale
+            for k, v in base.items():
+                setattr(a, k, v.data_ptr())
+            a.comp_kv, a.comp_rows, a.swa_rows = kv.data_ptr(), h.comp_kv.shape[0], h.swa.shape[0]
+            a.out, a.lse, a.err = out.data_ptr(), lse.data_ptr(), err.data_ptr()
+            hargs.append(a)
+        hws = B.step_workspace(hargs[0], dev)
+        g = R.capture([(lambda a=a: B.csa_decode_step(a, hws)) for a in hargs])
         ms = R.replays(g, nl, 20)
         torch.cuda.synchronize()
-        # the same positions are replayed: the appends repeat the same rows
-        # and may flag the n_comp bookkeeping; only range errors count here
-        if int(perr.item()) & ~0x4:
-            raise RuntimeError(f"producer: device error word {int(perr.item()):#x}")
-        wbytes = (2 * pinp.hd + 2 * pinp.ihd) * pinp.H * 2
-        pb = wbytes + T * (pinp.H * 2 + (2 * pinp.hd + 2 * pinp.ihd) * 4 + pinp.hd * 2)
-        r = {"step_us": _dist_us(ms), "min_bytes": pb}
-        r["gbs"] = round(pb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
+        if int(err.item()) != 0:
+            raise RuntimeError(f"hca_1m: device error word {int(err.item()):#x}")
+        rows = 8192 + 128
+        hb = rows * h.head_dim * 2 + 2 * h.n_heads * h.head_dim * 2
+        r = {"step_us": _dist_us(ms), "min_bytes": hb}
+        r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
+        r["gbs"] = round(hb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
         r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
-        r["workload"] = (f"producer of one decode step, {T} token(s): both compressors' "
-                         "projections (H 7168 -> 2x512 + 2x128), ring, window append, pooling")
-        res[f"producer_{T}"] = r
-        del wks, wis, g, st, pws
+        r["workload"] = "dense HCA decode step at 1M: 8192 ratio-128 blocks + 128 SWA rows, 64 x 512"
+        res["hca_1m"] = r
+        del kvs, hargs, hws, g
         torch.cuda.empty_cache()
-
-    # dense HCA at 1M
-    log("config: dense HCA step at 1M")
-    h = gen.hca1m()
-    nl = 60  # 60 x 8.5 MB of rows: well past the last-level cache
-
-    def tdev(a, dt):
-        return torch.as_tensor(a).to(dev) if dt is None else torch.as_tensor(a, dtype=dt).to(dev)
-
-    bf = lambda a: torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)  # noqa: E731
-    base = {"q": bf(h.q), "swa": bf(h.swa), "pos": tdev(h.pos, torch.int64),
-            "seq_kv": tdev(h.seq_kv, torch.int64), "n_comp": tdev(h.n_comp, torch.int32),
-            "swa_row0": tdev(h.swa_row0, torch.int64), "swa_len": tdev(h.swa_len, torch.int32)}
-    kv0 = bf(h.comp_kv)
-    kvs = [kv0] + [kv0.clone() for _ in range(nl - 1)]
-    out = torch.zeros((h.T, h.n_heads, h.head_dim), dtype=torch.bfloat16, device=dev)
-    lse = torch.zeros((h.T, h.n_heads), dtype=torch.float32, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    hargs = []
-    for kv in kvs:
-        a = B.StepArgs()
-        a.mode, a.T, a.ratio, a.window = B.CSA_MODE_HCA, h.T, h.ratio, 128
-        a.n_heads, a.head_dim, a.max_vis, a.scale = h.n_heads, h.head_dim, 8192, h.scale
-        for k, v in base.items():
-            setattr(a, k, v.data_ptr())
-        a.comp_kv, a.comp_rows, a.swa_rows = kv.data_ptr(), h.comp_kv.shape[0], h.swa.shape[0]
-        a.out, a.lse, a.err = out.data_ptr(), lse.data_ptr(), err.data_ptr()
-        hargs.append(a)
-    hws = B.step_workspace(hargs[0], dev)
-    g = R.capture([(lambda a=a: B.csa_decode_step(a, hws)) for a in hargs])
-    ms = R.replays(g, nl, 20)
-    torch.cuda.synchronize()
-    if int(err.item()) != 0:
-        raise RuntimeError(f"hca_1m: device error word {int(err.item()):#x}")
-    rows = 8192 + 128
-    hb = rows * h.head_dim * 2 + 2 * h.n_heads * h.head_dim * 2
-    r = {"step_us": _dist_us(ms), "min_bytes": hb}
-    r["steps_per_s"] = round(1e6 / r["step_us"]["median"], 1)
-    r["gbs"] = round(hb / (r["step_us"]["median"] * 1e-6) / 1e9, 1)
-    r["frac"] = round(r["gbs"] / HBM_PEAK_GBS, 4)
-    r["workload"] = "dense HCA decode step at 1M: 8192 ratio-128 blocks + 128 SWA rows, 64 x 512"
-    res["hca_1m"] = r
-    del kvs, hargs, hws, g
-    torch.cuda.empty_cache()
     return res
 
 
