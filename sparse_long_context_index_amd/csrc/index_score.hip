@@ -916,9 +916,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int LPT = TILE_CHUNKS / 64;   // DMA instructions (1 KiB) per tile: one per wave p < LPT
   static_assert(LPT <= kWaves, "one DMA instruction per wave and tile");
   constexpr int kMaxTiles = kGemmGroups * kMaxTpw;
-  __shared__ __attribute__((aligned(16))) u32x4 ring[kGemmSlots][TILE_CHUNKS];
-  __shared__ float s_sc[kWaves][kMaxTiles * kTileN];
+  // the key ring, then each wave's scores; before the first key DMA the same
+  // bytes stage the eight tokens' query rows (QB bytes a wave)
+  constexpr int RING_B = kGemmSlots * TILE_CHUNKS * 16;
+  constexpr int SC_B = kWaves * kMaxTiles * kTileN * 4;
+  constexpr int QB = MT * 32 * RB;
+  static_assert(kWaves * QB <= RING_B + SC_B, "query staging fits the ring and score space");
+  __shared__ __attribute__((aligned(16))) char lds_main[RING_B + SC_B];
   __shared__ int64_t s_nvis[kWaves];
+  u32x4 (*ring)[TILE_CHUNKS] = reinterpret_cast<u32x4 (*)[TILE_CHUNKS]>(lds_main);
+  float (*s_sc)[kMaxTiles * kTileN] = reinterpret_cast<float (*)[kMaxTiles * kTileN]>(lds_main + RING_B);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -927,25 +934,48 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = tw < T ? tw : T - 1;
   const int t0 = blockIdx.y * kWaves;          // its key rows serve the workgroup
 
-  // one round trip: the metadata, the queries (MFMA A operands: lane (col,
-  // half) holds head mt*32 + col, elements 16s + 8*half .. +8) and weights
+  // The token's query rows go to LDS by DMA, 1 KiB per instruction (chunk p
+  // of row r at position p ^ (r % CPR), as in the key tiles), and are read
+  // from there in the MFMA A layout (lane (col, half) holds head mt*32 + col,
+  // elements 16s + 8*half .. +8): loaded in that layout straight from memory,
+  // each instruction would touch 32 rows 32 B apiece, and those loads held
+  // the workgroup's start for several thousand cycles.  One load a lane
+  // brings the head weights.  Both are in flight with the metadata.
+  char* qst = lds_main + wave * QB;
+  {
+    const char* qsrc = reinterpret_cast<const char*>(q_idx + (int64_t)t * n_ih * IHD);
+    const int q_chunks = n_ih * CPR;
+    for (int e0 = 0; e0 < q_chunks; e0 += 64) {
+      const int c = min(e0 + lane, q_chunks - 1);  // the LDS chunk e0 + lane (past the rows: a copy)
+      const int r = c / CPR, p = (c % CPR) ^ (r & (CPR - 1));
+      lds_dma16_untracked(qsrc + (r * CPR + p) * 16, qst + e0 * 16);
+    }
+  }
+  const float wl = w[(int64_t)t * n_ih + min(lane, n_ih - 1)];
   const int64_t pos_t = pos[t];
   const int32_t ncomp_t = n_comp[t];
   const int64_t row0_t = seq_kv[t];
   const int64_t row0 = seq_kv[t0];
+  // all the metadata and scalar arguments the first key DMAs need, in one
+  // round trip (the empty asm takes them as operands; otherwise the compiler
+  // sinks some of these loads to their first use, a round trip later)
+  asm volatile("" ::"s"(pos_t), "s"(ncomp_t), "s"(row0_t), "s"(row0), "s"(k_rows), "s"(ld),
+               "s"(ratio), "s"(tpw), "s"(n_groups), "s"(T));
+  wait_vmcnt<0>();  // the query DMAs (not counted by the compiler) and the weights
   u32x4 qa[MT][KS];
   float wv[MT][16];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int hq = mt * 32 + col < n_ih ? mt * 32 + col : n_ih - 1;
-    const uint16_t* qrow = q_idx + ((int64_t)t * n_ih + hq) * IHD;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qrow + (2 * s + half) * 8);
+    for (int s = 0; s < KS; ++s)
+      qa[mt][s] = *reinterpret_cast<const u32x4*>(qst + (hq * CPR + ((2 * s + half) ^ (hq & (CPR - 1)))) * 16);
+    // heads past n_ih (their query rows repeat the last head's) weigh zero
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hw = mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      wv[mt][r] = w[(int64_t)t * n_ih + (hw < n_ih ? hw : n_ih - 1)];
-      if (hw >= n_ih) wv[mt][r] = 0.0f;
+      const float v = __shfl(wl, hw < n_ih ? hw : 0);
+      wv[mt][r] = hw < n_ih ? v : 0.0f;
     }
   }
   uint32_t flags = 0;
