@@ -252,10 +252,14 @@ typedef struct csa_step_args {
   const float* k_idx_scale;
   /* 1: every token's key rows start at the same seq_kv (one sequence, e.g. a
      prefill chunk), which lets S1 score the tokens as one GEMM whose key
-     tiles serve several tokens at once (bf16 indexer, T >= 64).  A token
+     tiles serve several tokens at once.  That form is taken for the bf16
+     indexer with T >= 64, n_ih <= 64, ihd 64 or 128, per-wave candidate
+     lists (not merged per workgroup), and rows too long for the batch
+     indexer (which takes up to 512 tokens whose rows fit one tile a wave);
+     otherwise the promise changes nothing.  Under the GEMM form a token
      whose seq_kv differs from that of the first token of its group of
-     eight then scores no block and raises CSA_DERR_BAD_META.  0: no
-     assumption.  Other values: CSA_EINVAL. */
+     eight (tokens 8g .. 8g+7) scores no block, selects nothing, and raises
+     CSA_DERR_BAD_META.  0: no assumption.  Other values: CSA_EINVAL. */
   int one_sequence;
 } csa_step_args;
 

@@ -1126,9 +1126,16 @@ hipError_t launch_gemm_ihd(const IndexScoreLaunch& a, const IndexPlan& p, hipStr
 
 }  // namespace
 
+// The batch kernel takes batches of short rows (one tile a wave), also of
+// one sequence; the GEMM form the rest of one_seq's launches it can run.
+static bool uses_batch_indexer(const IndexScoreLaunch& a, const IndexPlan& p) {
+  return batch_indexer(a.T, a.n_ih, a.ihd, a.e4m3) && p.tiles_per_wave == 1 &&
+         (a.cand.cand == nullptr || !a.cand.merge);
+}
+
 bool gemm_indexer(const IndexScoreLaunch& a) {
   return a.one_seq && !a.e4m3 && a.T >= kGemmMinT && a.n_ih <= 64 && (a.ihd == 64 || a.ihd == 128) &&
-         (a.cand.cand == nullptr || !a.cand.merge);
+         (a.cand.cand == nullptr || !a.cand.merge) && !uses_batch_indexer(a, plan_index(a.T, a.ld));
 }
 
 IndexPlan plan_index(int T, int64_t ld) {
@@ -1156,10 +1163,7 @@ IndexPlan plan_index(int T, int64_t ld) {
 hipError_t launch_index_score(const IndexScoreLaunch& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const IndexPlan bp = plan_index(a.T, a.ld);
-  if (batch_indexer(a.T, a.n_ih, a.ihd, a.e4m3) && bp.tiles_per_wave == 1 &&
-      (a.cand.cand == nullptr || !a.cand.merge)) {
-    return a.ihd == 64 ? launch_batch_ihd<64>(a, s) : launch_batch_ihd<128>(a, s);
-  }
+  if (uses_batch_indexer(a, bp)) return a.ihd == 64 ? launch_batch_ihd<64>(a, s) : launch_batch_ihd<128>(a, s);
   const IndexPlan& p = bp;
   if (gemm_indexer(a)) return a.ihd == 64 ? launch_gemm_ihd<64>(a, p, s) : launch_gemm_ihd<128>(a, p, s);
   switch (a.ihd) {

@@ -52,13 +52,13 @@ def test_prefill_one_sequence_matches_per_token_indexer_and_oracle(dev):
     check_step(inp, gemm, tokens=tokens[::9])
 
 
-def _two_sequences(split, seed, n_ih=64, ihd=128, T=640, base=(4096, 3000)):
+def _two_sequences(split, seed, n_ih=64, ihd=128, T=640, base=(4096, 3000), top_k=256):
     # tokens [0, split) of sequence 0, [split, T) of sequence 1, consecutive
     # positions in each from base[0] and base[1]
     pos = np.concatenate([base[0] + np.arange(split), base[1] + np.arange(T - split)])
     return gen.synth(seed, pos=pos, seq_of_token=[0] * split + [1] * (T - split),
                      n_comp_seq=[base[0] // 4 + split // 4 + 1, base[1] // 4 + (T - split) // 4 + 1],
-                     n_ih=n_ih, ihd=ihd, ratio=4, top_k=256, window=64, n_heads=16,
+                     n_ih=n_ih, ihd=ihd, ratio=4, top_k=top_k, window=64, n_heads=16,
                      head_dim=128, w_std=1.0 / np.sqrt(n_ih), swa_mode="per_token")
 
 
@@ -80,6 +80,23 @@ def test_one_sequence_broken_inside_a_workgroup(dev):
     _same_visible_scores(gemm, tok, inp, good)
     np.testing.assert_array_equal(gemm["count"][good], tok["count"][good])
     np.testing.assert_array_equal(gemm["idx"][good], tok["idx"][good])
+
+
+def test_one_sequence_with_short_rows_takes_the_batch_indexer(dev):
+    """64 tokens whose rows are short take the batch indexer even with the
+    promise: a token of another sequence is then scored on its own rows, and
+    the select does not drop it (no BAD_META; every output as without the
+    promise)."""
+    say("one_sequence with short rows: 64 tokens, batch indexer, split at token 61")
+    inp = _two_sequences(61, 74, T=64, top_k=128)
+    a = _run(inp, dev, True)
+    b = _run(inp, dev, False)
+    assert a["err"] == 0 and b["err"] == 0
+    _same_visible_scores(a, b, inp, range(inp.T))
+    np.testing.assert_array_equal(a["count"], b["count"])
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    assert (a["count"][61:] > 0).all()
 
 
 @pytest.mark.parametrize("n_ih,ihd", [(32, 64), (20, 128)])
