@@ -25,13 +25,13 @@ def B():
     return binding
 
 
-def _run(inp, dev, noalloc, e4m3=False):
+def _run(inp, dev, noalloc, e4m3=False, one_sequence=False):
     b = B()
     d = b.upload(inp, dev)
     if e4m3:
         d = b.quantize_indexer_e4m3(d)
     outs = b.alloc_step_outputs(inp, dev)
-    a = b.step_args(inp, d, outs, e4m3=e4m3)
+    a = b.step_args(inp, d, outs, e4m3=e4m3, one_sequence=one_sequence)
     if noalloc:
         b.csa_decode_step_noalloc(a)
     else:
@@ -70,6 +70,18 @@ def test_noalloc_batched_and_e4m3(dev):
     bat, tiny = gen.batched(), gen.tiny()
     _same(_run(bat, dev, True), _run(bat, dev, False), "batched")
     _same(_run(tiny, dev, True, e4m3=True), _run(tiny, dev, False, e4m3=True), "tiny E4M3")
+
+
+def test_noalloc_gemm_indexer(dev):
+    """The GEMM form of the indexer (640 tokens of one sequence, rows of about
+    13,160 blocks, one_sequence set) through the allocation-free step."""
+    say("csa_decode_step_noalloc: 640 tokens of one sequence, GEMM indexer")
+    T = 640
+    inp = gen.synth(11, pos=52000 + np.arange(T), seq_of_token=[0] * T,
+                    n_comp_seq=[52000 // 4 + T // 4 + 1], n_ih=64, ihd=128, ratio=4, top_k=256,
+                    window=64, n_heads=16, head_dim=128, w_std=0.125, swa_mode="per_token")
+    _same(_run(inp, dev, True, one_sequence=True), _run(inp, dev, False, one_sequence=True),
+          "GEMM indexer")
 
 
 def test_noalloc_rejects_oversized_steps(dev):
