@@ -99,6 +99,27 @@ def test_one_sequence_with_short_rows_takes_the_batch_indexer(dev):
     assert (a["count"][61:] > 0).all()
 
 
+def test_gemm_indexer_four_tile_groups(dev):
+    """64 tokens of one sequence over about 75,000 blocks: batches of up to
+    512 tokens plan four tiles a wave, so the GEMM kernel's groups are four
+    tiles (two steps) and its lists six keys (top_k 512: per-wave lists,
+    not merged).  Bit-equal to the per-token indexer; scores and top-k of
+    three tokens against the oracle."""
+    say("GEMM indexer, four-tile groups: 64 tokens, ~75K blocks, top_k 512")
+    inp = _two_sequences(64, 75, T=64, top_k=512, base=(300000, 0))
+    gemm = _run(inp, dev, True)
+    tok = _run(inp, dev, False)
+    assert gemm["err"] == 0 and tok["err"] == 0
+    _same_visible_scores(gemm, tok, inp, range(inp.T))
+    np.testing.assert_array_equal(gemm["count"], tok["count"])
+    np.testing.assert_array_equal(gemm["idx"], tok["idx"])
+    np.testing.assert_array_equal(gemm["out"], tok["out"])
+    for t in (0, 37, 63):
+        n, I, A = ref_scores(inp, t)
+        check_scores(gemm["scores"][t, :n], I, A, f"scores t={t}")
+        check_topk(gemm["idx"][t], int(gemm["count"][t]), I, A, inp.top_k, f"top-k t={t}")
+
+
 @pytest.mark.parametrize("n_ih,ihd", [(32, 64), (20, 128)])
 def test_gemm_indexer_other_shapes(dev, n_ih, ihd):
     """The GEMM indexer's other instantiations (32 heads or fewer; 64-wide
