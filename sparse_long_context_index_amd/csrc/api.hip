@@ -426,16 +426,21 @@ csa_status run_step(const csa_step_args* a, void* ws, size_t ws_bytes, void* str
     P.top_k = C;
     P.idx = reinterpret_cast<int32_t*>(base + lay.pre_idx);
     P.count = reinterpret_cast<int32_t*>(base + lay.pre_count);
-    e = launch_step_select(P, a->T, st);
-    if (e != hipSuccess) return hip_status(e);
     RescoreLaunch R{};
     R.q_idx = a->q_idx; R.w = a->w; R.k_idx = a->k_idx; R.seq_kv = a->seq_kv;
     R.idx = P.idx; R.count = P.count;
     R.T = a->T; R.n_ih = a->n_ih; R.ihd = a->ihd; R.C = C;
     R.key = reinterpret_cast<uint64_t*>(base + lay.pre_key);
     R.gcut = reinterpret_cast<uint64_t*>(base + lay.pre_gcut);
-    e = launch_rescore(R, st);
-    if (e != hipSuccess) return hip_status(e);
+    if (prefilter_rescore_fits(R)) {
+      e = launch_prefilter_rescore(P, R, a->T, st);
+      if (e != hipSuccess) return hip_status(e);
+    } else {
+      e = launch_step_select(P, a->T, st);
+      if (e != hipSuccess) return hip_status(e);
+      e = launch_rescore(R, st);
+      if (e != hipSuccess) return hip_status(e);
+    }
     S.cand = R.key; S.gcut = R.gcut; S.list_len = C;
     S.groups_per_token = 1; S.blocks_per_group = (int)a->max_vis; S.lists_complete = 1;
   }

@@ -374,6 +374,14 @@ struct RescoreLaunch {
   uint64_t* key; uint64_t* gcut;
 };
 hipError_t launch_rescore(const RescoreLaunch& a, hipStream_t s);
+// The prefilter's select (S with top_k = C, whose idx and count it does not
+// write) fused with the rescore of its candidates: one launch instead of
+// launch_step_select + launch_rescore, for up to 64 indexer heads and ihd 64
+// or 128 (prefilter_rescore_fits).
+bool prefilter_rescore_fits(const RescoreLaunch& a);
+struct SelectLaunch;
+hipError_t launch_prefilter_rescore(const SelectLaunch& sl, const RescoreLaunch& a, int T,
+                                    hipStream_t s);
 // The producer side of one decode step (produce.hip): both compressors'
 // projections of the new tokens, the ring of recent projections, the
 // sliding-window append and, at block ends, the pooled compressed rows.

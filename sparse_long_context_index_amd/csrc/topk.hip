@@ -106,6 +106,110 @@ __global__ __launch_bounds__(kCandThreads) void score_cands_kernel(
   cand_publish(val, n_ok, ca, t, wave_in_token, blockIdx.x, lds, kStride);
 }
 
+// The E4M3 prefilter and its bf16 rescore in one launch.  Workgroup x of
+// token t runs the exact select of the C best blocks by E4M3 score (every
+// workgroup of the token reaches the same selection) but keeps only its
+// positions [128x, 128x + 128) of the ascending block order; four of its
+// waves then rescore those, 32 a wave, as rescore_kernel does (lane (col,
+// half) reads its candidate's bf16 key row into the B operand registers;
+// the same operations in the same order as the bf16 indexer, so a score is
+// that indexer's score of the block), with the query block and weights in
+// LDS.  Against a select kernel of one workgroup a token and the rescore
+// launch after it: one kernel boundary and one round trip fewer.
+constexpr int kRescorePerWg = 128;
+template <int IHD, int MT, int KP>
+__global__ __launch_bounds__(sel::kThreads) void prefilter_rescore_kernel(SelectLaunch sl,
+                                                                        RescoreLaunch a) {
+  constexpr int KS = IHD / 16;
+  constexpr int RB = 2 * IHD;
+  constexpr int CPR = RB / 16;
+  constexpr int QCH = MT * 32 * CPR;
+  __shared__ union {
+    sel::SelShared<sel::kThreads> s;
+    sel::FastShared<sel::kThreads> f;
+  } u;
+  __shared__ int32_t cand[kRescorePerWg];
+  __shared__ __attribute__((aligned(16))) u32x4 qlds[QCH];
+  __shared__ float wl[MT * 32];
+  const int t = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  // the query rows (chunk p of row r at slot r*CPR + (p ^ (r % CPR)); rows
+  // past n_ih repeat the last head, whose weight here is zero) and weights
+  const char* qt = reinterpret_cast<const char*>(a.q_idx) + (int64_t)t * a.n_ih * RB;
+  for (int e = tid; e < QCH; e += sel::kThreads) {
+    const int r = e / CPR, pp = e % CPR;
+    const int hq = r < a.n_ih ? r : a.n_ih - 1;
+    qlds[r * CPR + (pp ^ (r & (CPR - 1)))] = *reinterpret_cast<const u32x4*>(qt + (int64_t)hq * RB + pp * 16);
+  }
+  if (tid < MT * 32) wl[tid] = tid < a.n_ih ? a.w[(int64_t)t * a.n_ih + tid] : 0.0f;
+  const uint32_t e_lo = blockIdx.x * kRescorePerWg;
+  const sel::SelResult r = sel::step_select<sel::kThreads, KP>(
+      sl.scores + (int64_t)t * sl.ld, sl.ld, sl.pos[t], sl.n_comp[t], sl.ratio, select_row0(sl, t),
+      sl.k_rows, sl.top_k, sl.cand + (int64_t)t * sl.groups_per_token * sl.list_len,
+      sl.gcut + (int64_t)t * sl.groups_per_token, sl.list_len, sl.groups_per_token,
+      sl.blocks_per_group, sl.lists_complete != 0, u.f, u.s, cand, e_lo, e_lo + kRescorePerWg);
+  __syncthreads();  // this workgroup's candidates, the queries and weights are in LDS
+  if (blockIdx.x == 0 && tid == 0) {
+    a.gcut[t] = 0ull;
+    report(sl.err, r.flags);
+  }
+  if (wave >= kRescorePerWg / 32) return;
+  const int64_t j0 = (int64_t)e_lo + wave * 32;
+  if (j0 >= a.C) return;  // wave-uniform
+  const int64_t j = j0 + col;
+  uint64_t* out = a.key + (int64_t)t * a.C;
+  const int64_t cnt = r.emitted;
+  if (j0 >= cnt) {  // wave-uniform: no candidate in this tile
+    if (half == 0 && j < a.C) out[j] = 0ull;
+    return;
+  }
+  // lanes past the count take the tile's first candidate (j0 < cnt)
+  const bool valid = j < cnt;
+  const int64_t pj = valid ? j : j0;
+  const int32_t b = r.listed ? cand[pj - e_lo] : (int32_t)pj;
+  const char* krow = reinterpret_cast<const char*>(a.k_idx) + (a.seq_kv[t] + b) * RB;
+  u32x4 kb[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kb[s] = *reinterpret_cast<const u32x4*>(krow + (2 * s + half) * 16);
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int qr = mt * 32 + col;
+      const u32x4 qa = qlds[qr * CPR + ((2 * s + half) ^ (qr & (CPR - 1)))];
+      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa),
+                                                        __builtin_bit_cast(bf16x8, kb[s]), acc[mt],
+                                                        0, 0, 0);
+    }
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      part += wl[mt * 32 + 8 * (rr >> 2) + 4 * half + (rr & 3)] * relu_f32(acc[mt][rr]);
+  }
+  part += __shfl_xor(part, 32);
+  const uint32_t sk = score_key(part);
+  if (half == 0 && j < a.C)
+    out[j] = valid && sk != 0u ? ((uint64_t)sk << 32) | (uint32_t)~(uint32_t)b : 0ull;
+}
+
+template <int IHD, int MT>
+void launch_prefilter_rescore_t(const SelectLaunch& sl, const RescoreLaunch& a, int T, hipStream_t s) {
+  const dim3 grid((unsigned)((a.C + kRescorePerWg - 1) / kRescorePerWg), (unsigned)T);
+  // a batch may mix row lengths; a single row is the long row its lists serve
+  if (T > 1)
+    hipLaunchKernelGGL((prefilter_rescore_kernel<IHD, MT, 12>), grid, dim3(sel::kThreads), 0, s, sl, a);
+  else
+    hipLaunchKernelGGL((prefilter_rescore_kernel<IHD, MT, 4>), grid, dim3(sel::kThreads), 0, s, sl, a);
+}
+
 }  // namespace
 
 TopkPlan plan_topk(int T, int64_t ld, int top_k, int pool) {
@@ -206,6 +310,23 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int64_t* po
     hipLaunchKernelGGL((topk_select_kernel<sel::KPT>), dim3((unsigned)T), dim3(sel::kThreads), 0, s,
                        scores, ld, pos, n_comp, seq_kv, k_rows, ratio, top_k, ws.cand, ws.gcut, p.list_len,
                        p.groups_per_token, p.blocks_per_group, idx, count, err);
+  return hipGetLastError();
+}
+
+bool prefilter_rescore_fits(const RescoreLaunch& a) {
+  return a.C > 0 && a.n_ih <= 64 && (a.ihd == 64 || a.ihd == 128);
+}
+
+hipError_t launch_prefilter_rescore(const SelectLaunch& sl, const RescoreLaunch& a, int T,
+                                    hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!prefilter_rescore_fits(a)) return hipErrorInvalidValue;
+  const bool one = a.n_ih <= 32;
+  if (a.ihd == 64) {
+    if (one) launch_prefilter_rescore_t<64, 1>(sl, a, T, s); else launch_prefilter_rescore_t<64, 2>(sl, a, T, s);
+  } else {
+    if (one) launch_prefilter_rescore_t<128, 1>(sl, a, T, s); else launch_prefilter_rescore_t<128, 2>(sl, a, T, s);
+  }
   return hipGetLastError();
 }
 
